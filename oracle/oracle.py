@@ -1,0 +1,231 @@
+"""ctypes wrapper around ``ra_oracle.c`` (test infrastructure only).
+
+Each wrapper names the step of the method it runs; the arithmetic itself lives
+in ``ra_oracle.c``, which documents the page passages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ra_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libra_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+ROT_NONE, ROT_INTERLEAVED, ROT_HALF = 0, 1, 2
+ROT_NAMES = {"none": ROT_NONE, "interleaved": ROT_INTERLEAVED, "half": ROT_HALF}
+BLOCK = 64
+
+__all__ = [
+    "build", "lib", "ROT_NONE", "ROT_INTERLEAVED", "ROT_HALF", "ROT_NAMES",
+    "BLOCK", "pgrid", "bf16_bits_to_f32", "as_f32", "rope_table", "rope_rotate",
+    "quant_qk", "quant_v", "prologue", "pmap_thresholds", "pmap",
+    "attention_rows", "attention_tile", "attention_full", "schedule_full_precision",
+    "set_threads", "get_threads",
+]
+
+
+def build(force: bool = False) -> str:
+    """Compile ra_oracle.c into libra_oracle.so next to it."""
+    if force or not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            L = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            i32, f64 = ctypes.c_int, ctypes.c_double
+            L.ora_pgrid.restype = i32
+            L.ora_block.restype = i32
+            L.ora_set_threads.argtypes = [i32]
+            L.ora_get_threads.restype = i32
+            L.ora_rope_table.argtypes = [i32, i32, f64, i32, P, P]
+            L.ora_rope_rotate.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, f64, i32]
+            L.ora_quant_qk.argtypes = [P, i32, i32, i32, i32, P, P]
+            L.ora_quant_v.argtypes = [P, i32, i32, i32, i32, P, P]
+            L.ora_pmap_thresholds.argtypes = [i32, P]
+            L.ora_pmap.argtypes = [P, ctypes.c_int64, P]
+            L.ora_attention_head.argtypes = [P, P, P, P, P, P, i32, i32, f64,
+                                             P, i32, P, P, i32, P, P, P, P]
+            L.ora_schedule_full_precision.argtypes = [i32] * 8
+            for name in ("ora_rope_table", "ora_rope_rotate", "ora_quant_qk",
+                         "ora_quant_v", "ora_pmap_thresholds", "ora_pmap",
+                         "ora_attention_head", "ora_schedule_full_precision"):
+                getattr(L, name).restype = i32
+            _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("oracle %s rejected its arguments (rc=%d)" % (what, rc))
+
+
+def pgrid() -> int:
+    """Steps per log2 unit of the grid on which the P exponent is rounded."""
+    return lib().ora_pgrid()
+
+
+def set_threads(n: int) -> None:
+    lib().ora_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return lib().ora_get_threads()
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16) to float32."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def as_f32(x: np.ndarray) -> np.ndarray:
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(bf16_bits_to_f32(x))
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def rope_table(npos: int, L: int, theta: float, rot: int):
+    cs = np.empty((npos, L // 2), np.float32)
+    sn = np.empty((npos, L // 2), np.float32)
+    _check(lib().ora_rope_table(npos, L, float(theta), int(rot), _p(cs), _p(sn)), "rope_table")
+    return cs, sn
+
+
+def rope_rotate(x, grid, seg, theta=10000.0, rot=ROT_HALF) -> np.ndarray:
+    """3D RoPE + RoPE-aware rotation of x [B, N, H, D] in binary32."""
+    x = as_f32(x)
+    B, N, H, D = x.shape
+    F, Hh, W = grid
+    assert N == F * Hh * W
+    y = np.empty_like(x)
+    seg_a = np.asarray(seg, dtype=np.int32)
+    _check(lib().ora_rope_rotate(_p(x), _p(y), B, H, D, F, Hh, W, _p(seg_a),
+                                 float(theta), int(rot)), "rope_rotate")
+    return y
+
+
+def quant_qk(y):
+    """Per-(b, h, 64-token block) symmetric INT4 -> codes [B,H,N,D], scales [B,H,nblk]."""
+    y = as_f32(y)
+    B, N, H, D = y.shape
+    nblk = (N + BLOCK - 1) // BLOCK
+    codes = np.empty((B, H, N, D), np.int8)
+    scales = np.empty((B, H, nblk), np.float32)
+    _check(lib().ora_quant_qk(_p(y), B, N, H, D, _p(codes), _p(scales)), "quant_qk")
+    return codes, scales
+
+
+def quant_v(v):
+    """Per-(b, h, channel) symmetric INT4 -> codes [B,H,N,D], scales [B,H,D]."""
+    v = as_f32(v)
+    B, N, H, D = v.shape
+    codes = np.empty((B, H, N, D), np.int8)
+    scales = np.empty((B, H, D), np.float32)
+    _check(lib().ora_quant_v(_p(v), B, N, H, D, _p(codes), _p(scales)), "quant_v")
+    return codes, scales
+
+
+def prologue(q, k, v, grid, seg, theta=10000.0, rot=ROT_HALF):
+    """RoPE + rotation + INT4 quantization of Q/K, and INT4 quantization of V."""
+    qr = rope_rotate(q, grid, seg, theta, rot)
+    kr = rope_rotate(k, grid, seg, theta, rot)
+    qc, sq = quant_qk(qr)
+    del qr
+    kc, sk = quant_qk(kr)
+    del kr
+    vc, sv = quant_v(v)
+    return dict(q_codes=qc, s_q=sq, k_codes=kc, s_k=sk, v_codes=vc, s_v=sv)
+
+
+def pmap_thresholds(G: int | None = None) -> np.ndarray:
+    tau = np.empty(15, np.int32)
+    _check(lib().ora_pmap_thresholds(int(G or pgrid()), _p(tau)), "pmap_thresholds")
+    return tau
+
+
+def pmap(x) -> np.ndarray:
+    """u = code + 8 for grid exponents x (binary32 values)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = np.empty(x.shape, np.uint8)
+    _check(lib().ora_pmap(_p(x), x.size, _p(u)), "pmap")
+    return u
+
+
+def _head(pro, b, h):
+    return (np.ascontiguousarray(pro["q_codes"][b, h]), np.ascontiguousarray(pro["s_q"][b, h]),
+            np.ascontiguousarray(pro["k_codes"][b, h]), np.ascontiguousarray(pro["s_k"][b, h]),
+            np.ascontiguousarray(pro["v_codes"][b, h]), np.ascontiguousarray(pro["s_v"][b, h]))
+
+
+def attention_rows(pro, b, h, rows, softmax_scale=None, with_m=False):
+    """Oracle output rows (binary64) of head (b, h) for query indices `rows`."""
+    qc, sq, kc, sk, vc, sv = _head(pro, b, h)
+    N, D = qc.shape
+    scale = float(softmax_scale) if softmax_scale else 1.0 / np.sqrt(D)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    o = np.empty((rows.size, D), np.float64)
+    m = np.empty(rows.size, np.float32)
+    _check(lib().ora_attention_head(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), N, D,
+                                    scale, _p(rows), rows.size, _p(o), _p(m), -1,
+                                    None, None, None, None), "attention_head")
+    return (o, m) if with_m else o
+
+
+def attention_tile(pro, b, h, q_blk, kv_blk, softmax_scale=None):
+    """Tile dump after key step kv_blk for the 64 query rows of q_blk.
+
+    Rows past N are absent; returns dict of s_int [r,64], p_code [r,64],
+    pv_int [r,D], m_after [r] for the valid rows r."""
+    qc, sq, kc, sk, vc, sv = _head(pro, b, h)
+    N, D = qc.shape
+    scale = float(softmax_scale) if softmax_scale else 1.0 / np.sqrt(D)
+    r0 = q_blk * BLOCK
+    rows = np.arange(r0, min(N, r0 + BLOCK), dtype=np.int32)
+    n = rows.size
+    o = np.empty((n, D), np.float64)
+    s_int = np.zeros((n, BLOCK), np.int32)
+    p_code = np.zeros((n, BLOCK), np.int8)
+    pv = np.zeros((n, D), np.int32)
+    m_after = np.zeros(n, np.float32)
+    _check(lib().ora_attention_head(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), N, D,
+                                    scale, _p(rows), n, _p(o), None, int(kv_blk),
+                                    _p(s_int), _p(p_code), _p(pv), _p(m_after)),
+           "attention_tile")
+    return dict(s_int=s_int, p_code=p_code, pv_int=pv, m_after=m_after)
+
+
+def attention_full(pro, softmax_scale=None):
+    """Oracle output [B, N, H, D] (binary64) for every row of every head."""
+    B, H, N, D = pro["q_codes"].shape
+    out = np.empty((B, N, H, D), np.float64)
+    rows = np.arange(N, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            out[b, :, h, :] = attention_rows(pro, b, h, rows, softmax_scale)
+    return out
+
+
+def schedule_full_precision(sched, step, n_steps, block, n_blocks) -> bool:
+    sh, st, bh, bt = sched
+    return bool(lib().ora_schedule_full_precision(sh, st, bh, bt, step, n_steps, block, n_blocks))

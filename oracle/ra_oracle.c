@@ -1,0 +1,401 @@
+/*
+ * ra_oracle.c -- plain CPU oracle for the RotateAttention INT4 attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header,
+ * table or constant generator with the HIP library; the two are written
+ * independently from the same method description.
+ *
+ * Source pages (cited by title and section):
+ *  [RA]  "RotateAttention: RoPE-Aware Rotation and Range Rectification for INT4
+ *        Quantized Attention in Video Generation" -- pith.science review page:
+ *        abstract, Sec. 3 / Fig. 2 (3D RoPE segments), Sec. 4.1 / Fig. 3
+ *        (Interleaved and Half rotations, H2 blocks, orthogonality argument),
+ *        Sec. 4.2 (range-optimized P: scale 15, zero-point -8), Sec. 5.1
+ *        (FP16 step/block fallback), free-parameter ledger.
+ *  [PARO] "PAROAttention" review page -- 64-token blocks aligned with the
+ *        FlashAttention tile (precedent for the Q/K quantization block).
+ *
+ * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ * Every float operation below is IEEE binary32 (or binary64 where stated) in
+ * the order written; -ffp-contract=off keeps a*b+c from being fused.
+ *
+ * Where the pages leave a step open, the reading taken is stated at the
+ * function that implements it.  Integer quantities (codes, scores, P codes,
+ * PV sums) are exact; the final normalisation is carried in binary64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+enum { ORA_ROT_NONE = 0, ORA_ROT_INTERLEAVED = 1, ORA_ROT_HALF = 2 };
+enum { ORA_BLOCK = 64 };      /* tokens per Q/K scale block and per key step */
+enum { ORA_CODE_MAX = 7 };    /* symmetric INT4 codes in [-7, 7] */
+enum { ORA_MAX_D = 256 };
+
+/* Steps per log2 unit of the exponent grid on which P is evaluated. */
+enum { ORA_PGRID = 4755 };
+
+int ora_pgrid(void) { return ORA_PGRID; }
+int ora_block(void) { return ORA_BLOCK; }
+
+void ora_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }
+int ora_get_threads(void) { return omp_get_max_threads(); }
+
+/* ------------------------------------------------------------------------ */
+/* 3D RoPE tables ([RA] Sec. 3, Fig. 2: head dims split into frame / height /
+ * width segments, each rotated by its own axis coordinate).
+ * Reading: adjacent pairs (2j, 2j+1) inside a segment of even length L;
+ * frequency theta^(-2j/L); positions start at 0.  With the Interleaved
+ * rotation merged ([RA] Sec. 4.1: "mergeable into RoPE"), each pair angle
+ * gains +pi/4, i.e. the 2x2 block R(pi/4) is composed with R(pos*freq).
+ * Angles in binary64, cos/sin rounded once to binary32.                     */
+static void seg_table(int npos, int L, double theta, int interleaved,
+                      float *cs, float *sn)
+{
+    int half = L / 2;
+    for (int p = 0; p < npos; ++p) {
+        for (int j = 0; j < half; ++j) {
+            double expo = (double)(-2 * j) / (double)L;
+            double freq = pow(theta, expo);
+            double ang = (double)p * freq;
+            if (interleaved) {
+                double quarter = M_PI / 4.0;
+                ang = ang + quarter;
+            }
+            cs[p * half + j] = (float)cos(ang);
+            sn[p * half + j] = (float)sin(ang);
+        }
+    }
+}
+
+/* Exported for table-equality tests: cos/sin of segment s (0 frame, 1 height,
+ * 2 width) laid out [pos][pair]. */
+int ora_rope_table(int npos, int L, double theta, int rot, float *cs, float *sn)
+{
+    if (npos < 1 || L < 2 || (L & 1)) return -1;
+    seg_table(npos, L, theta, rot == ORA_ROT_INTERLEAVED, cs, sn);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RoPE + RoPE-aware rotation of one token row x[D] -> y[D] (binary32).
+ * Pair rotation (a, b) -> (a c - b s, a s + b c), each product rounded, then
+ * the sum/difference rounded.
+ * Half rotation ([RA] Sec. 4.1 / Fig. 3: each dim paired with its counterpart
+ * in the other half of the segment; block H2 = (1/sqrt2)[[1,1],[1,-1]] by the
+ * free-parameter ledger) is applied after RoPE:
+ *   u' = (u + w) r,  w' = (u - w) r,  r = binary32(1/sqrt2).                 */
+static void rotate_row(const float *x, float *y, int D, const int *seg,
+                       const int *pos, float *const *cs, float *const *sn,
+                       int rot)
+{
+    float tmp[ORA_MAX_D];
+    const float r = (float)M_SQRT1_2;
+    int off = 0;
+    for (int s = 0; s < 3; ++s) {
+        int L = seg[s], half = L / 2;
+        const float *c = cs[s] + (size_t)pos[s] * half;
+        const float *sv = sn[s] + (size_t)pos[s] * half;
+        for (int j = 0; j < half; ++j) {
+            float a = x[off + 2 * j], b = x[off + 2 * j + 1];
+            float ac = a * c[j], bs = b * sv[j];
+            float as = a * sv[j], bc = b * c[j];
+            tmp[off + 2 * j] = ac - bs;
+            tmp[off + 2 * j + 1] = as + bc;
+        }
+        if (rot == ORA_ROT_HALF) {
+            for (int i = 0; i < half; ++i) {
+                float u = tmp[off + i], w = tmp[off + i + half];
+                float sum = u + w, dif = u - w;
+                y[off + i] = sum * r;
+                y[off + i + half] = dif * r;
+            }
+        } else {
+            for (int i = 0; i < L; ++i) y[off + i] = tmp[off + i];
+        }
+        off += L;
+    }
+}
+
+/* x, y: [B, N, H, D] binary32.  Token n -> (f, h, w) in row-major order with
+ * w fastest (N = F*Hh*W).  rot: 0 none, 1 interleaved (merged), 2 half. */
+int ora_rope_rotate(const float *x, float *y, int B, int H, int D,
+                    int F, int Hh, int W, const int *seg, double theta, int rot)
+{
+    if (D > ORA_MAX_D || seg[0] + seg[1] + seg[2] != D) return -1;
+    for (int s = 0; s < 3; ++s) if (seg[s] < 2 || (seg[s] & 1)) return -1;
+    if (rot < 0 || rot > 2) return -1;
+    int dims[3] = {F, Hh, W};
+    float *cs[3], *sn[3];
+    for (int s = 0; s < 3; ++s) {
+        size_t n = (size_t)dims[s] * (seg[s] / 2);
+        cs[s] = (float *)malloc(n * sizeof(float));
+        sn[s] = (float *)malloc(n * sizeof(float));
+        seg_table(dims[s], seg[s], theta, rot == ORA_ROT_INTERLEAVED, cs[s], sn[s]);
+    }
+    long N = (long)F * Hh * W;
+    #pragma omp parallel for schedule(static)
+    for (long bn = 0; bn < (long)B * N; ++bn) {
+        long n = bn % N;
+        int pos[3];
+        pos[0] = (int)(n / ((long)Hh * W));
+        pos[1] = (int)((n / W) % Hh);
+        pos[2] = (int)(n % W);
+        for (int h = 0; h < H; ++h) {
+            size_t o = ((size_t)bn * H + h) * D;
+            rotate_row(x + o, y + o, D, seg, pos, cs, sn, rot);
+        }
+    }
+    for (int s = 0; s < 3; ++s) { free(cs[s]); free(sn[s]); }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Symmetric INT4 quantizer of one group ([RA] abstract: INT4 Q and K).
+ * Reading: codes in [-7, 7]; scale = amax / 7; code = RNE(x * (7 / amax)),
+ * clamped; an all-zero group gets scale 0 and codes 0.                     */
+static float group_scale(float amax, float *inv)
+{
+    if (amax == 0.0f) { *inv = 0.0f; return 0.0f; }
+    *inv = 7.0f / amax;
+    return amax / 7.0f;
+}
+
+static int8_t quant_one(float x, float inv)
+{
+    float t = x * inv;
+    float q = rintf(t);
+    if (q > (float)ORA_CODE_MAX) q = (float)ORA_CODE_MAX;
+    if (q < -(float)ORA_CODE_MAX) q = -(float)ORA_CODE_MAX;
+    return (int8_t)q;
+}
+
+/* Q/K: one scale per (b, h, 64-token block) over the valid tokens x all D
+ * channels (reading of the per-(head, 64-token block) granularity; [PARO]
+ * uses the same 64-block tile).  y: [B, N, H, D]; codes: [B, H, N, D];
+ * scales: [B, H, ceil(N/64)]. */
+int ora_quant_qk(const float *y, int B, int N, int H, int D,
+                 int8_t *codes, float *scales)
+{
+    int nblk = (N + ORA_BLOCK - 1) / ORA_BLOCK;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            for (int blk = 0; blk < nblk; ++blk) {
+                int n0 = blk * ORA_BLOCK;
+                int n1 = n0 + ORA_BLOCK < N ? n0 + ORA_BLOCK : N;
+                float amax = 0.0f;
+                for (int n = n0; n < n1; ++n)
+                    for (int d = 0; d < D; ++d) {
+                        float a = fabsf(y[(((size_t)b * N + n) * H + h) * D + d]);
+                        if (a > amax) amax = a;
+                    }
+                float inv;
+                float s = group_scale(amax, &inv);
+                scales[((size_t)b * H + h) * nblk + blk] = s;
+                for (int n = n0; n < n1; ++n)
+                    for (int d = 0; d < D; ++d) {
+                        float v = y[(((size_t)b * N + n) * H + h) * D + d];
+                        codes[(((size_t)b * H + h) * N + n) * D + d] =
+                            (s == 0.0f) ? 0 : quant_one(v, inv);
+                    }
+            }
+        }
+    return 0;
+}
+
+/* V: one scale per (b, h, channel) over all N tokens (per-channel symmetric
+ * INT4).  v: [B, N, H, D]; codes: [B, H, N, D]; scales: [B, H, D]. */
+int ora_quant_v(const float *v, int B, int N, int H, int D,
+                int8_t *codes, float *scales)
+{
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            for (int d = 0; d < D; ++d) {
+                float amax = 0.0f;
+                for (int n = 0; n < N; ++n) {
+                    float a = fabsf(v[(((size_t)b * N + n) * H + h) * D + d]);
+                    if (a > amax) amax = a;
+                }
+                float inv;
+                float s = group_scale(amax, &inv);
+                scales[((size_t)b * H + h) * D + d] = s;
+                for (int n = 0; n < N; ++n) {
+                    float x = v[(((size_t)b * N + n) * H + h) * D + d];
+                    codes[(((size_t)b * H + h) * N + n) * D + d] =
+                        (s == 0.0f) ? 0 : quant_one(x, inv);
+                }
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Range-optimized P map ([RA] Sec. 4.2: fixed scale 15, zero-point -8, so
+ * p in [0,1] covers the whole signed INT4 range [-8, 7]).
+ * code = round(15 p) - 8, p = 2^(x/G) with x the integer exponent on the grid
+ * of G steps per log2 unit.  Rounding is half-up; u = code + 8 in [0, 15].
+ * Written as a count of thresholds: u = #{k in 0..14 : x >= tau_k}, where
+ * tau_k is the smallest integer with 15 * 2^(tau_k/G) >= k + 1/2.           */
+int ora_pmap_thresholds(int G, int32_t *tau)
+{
+    if (G < 1) return -1;
+    for (int k = 0; k < 15; ++k) {
+        long double target = (long double)k + 0.5L;
+        long double t = log2l((long double)(2 * k + 1) / 30.0L) * (long double)G;
+        long x = (long)ceill(t);
+        while (15.0L * exp2l((long double)x / G) < target) ++x;
+        while (15.0L * exp2l((long double)(x - 1) / G) >= target) --x;
+        tau[k] = (int32_t)x;
+    }
+    return 0;
+}
+
+static int pmap_u(float x, const int32_t *tau)
+{
+    int u = 0;
+    for (int k = 0; k < 15; ++k)
+        if (x >= (float)tau[k]) ++u;
+    return u;
+}
+
+/* Vectorised form for tests: u[i] = map(x[i]) with the oracle's grid. */
+int ora_pmap(const float *x, int64_t n, uint8_t *u)
+{
+    int32_t tau[15];
+    ora_pmap_thresholds(ORA_PGRID, tau);
+    for (int64_t i = 0; i < n; ++i) u[i] = (uint8_t)pmap_u(x[i], tau);
+    return 0;
+}
+
+/* Smallest binary32 value >= the exact product s * c (s integer, |s| < 2^24). */
+static float mul_round_up(int32_t s, float c)
+{
+    double exact = (double)s * (double)c;        /* exact: 24 + 24 bits */
+    float m = (float)exact;
+    if ((double)m < exact) m = nextafterf(m, INFINITY);
+    return m;
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT4 attention for one (b, h) slice, on selected query rows.
+ *
+ * Online softmax over key steps of 64 keys in ascending order (reading of
+ * P = exp(QK - max(QK)) [RA abstract] inside a FlashAttention loop: the max
+ * is the running max, updated once per 64-key step).
+ *   scores     S = sum_d qhat kc                               (exact int)
+ *   c          = f32(f32(s_q s_k) * alphaG),
+ *              alphaG = f32(log2(e) * softmax_scale * G)       (log2 units * G)
+ *   step max   m_t = smallest f32 >= max_j(S_j) * c;  m = max(m, m_t)
+ *   exponent   x_j = RNE(f32(S_j c - m))  (single rounding of the exact value)
+ *   P code     u_j = #{k : x_j >= tau_k}  in [0, 15]; code = u - 8
+ *   sums       U = sum_j u_j;  num_c = sum_j u_j vhat_jc;
+ *              PV_c = sum_j code_j vhat_jc = num_c - 8 sum_j vhat_jc
+ *   float path (binary64):  beta = 2^((m_old - m)/G),
+ *              A = A beta + num,  L = L beta + U,  o = A s_v / L.
+ * The dequantized P is u/15, so the 1/15 cancels in A/L: the row is
+ * normalised by the sum of its quantized probabilities.
+ *
+ * qc, kc, vc: [N, D] int8 codes of this (b, h); sq, sk: [ceil(N/64)];
+ * sv: [D].  rows: nrows query indices; o: [nrows, D] binary64.
+ * m_out (optional): final running max per selected row (binary32).
+ * Tile dump (optional, dbg_kb >= 0): for selected rows, after key step dbg_kb,
+ * s_int[r*64 + j], p_code[r*64 + j] (-8 for keys >= N), pv_int[r*D + c],
+ * m_after[r], indexed by r = position of the row in `rows`.                 */
+int ora_attention_head(const int8_t *qc, const float *sq,
+                       const int8_t *kc, const float *sk,
+                       const int8_t *vc, const float *sv,
+                       int N, int D, double softmax_scale,
+                       const int32_t *rows, int nrows, double *o, float *m_out,
+                       int dbg_kb, int32_t *s_int, int8_t *p_code,
+                       int32_t *pv_int, float *m_after)
+{
+    if (D > ORA_MAX_D || N < 1) return -1;
+    int32_t tau[15];
+    ora_pmap_thresholds(ORA_PGRID, tau);
+    const float alphaG = (float)(M_LOG2E * softmax_scale * (double)ORA_PGRID);
+    int nkb = (N + ORA_BLOCK - 1) / ORA_BLOCK;
+
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r) {
+        int i = rows[r];
+        int qb = i / ORA_BLOCK;
+        const int8_t *qi = qc + (size_t)i * D;
+        float m = -INFINITY;
+        double A[ORA_MAX_D], L = 0.0;
+        int32_t S[ORA_BLOCK], u[ORA_BLOCK];
+        int64_t num[ORA_MAX_D];
+        for (int c = 0; c < D; ++c) A[c] = 0.0;
+
+        for (int kb = 0; kb < nkb; ++kb) {
+            int j0 = kb * ORA_BLOCK;
+            int nj = (j0 + ORA_BLOCK < N ? ORA_BLOCK : N - j0);
+            float sqk = sq[qb] * sk[kb];
+            float c = sqk * alphaG;
+
+            int32_t smax = INT32_MIN;
+            for (int j = 0; j < nj; ++j) {
+                const int8_t *kj = kc + (size_t)(j0 + j) * D;
+                int64_t acc = 0;
+                for (int d = 0; d < D; ++d) acc += (int64_t)qi[d] * kj[d];
+                S[j] = (int32_t)acc;
+                if (S[j] > smax) smax = S[j];
+            }
+            float mt = mul_round_up(smax, c);
+            float mnew = m > mt ? m : mt;
+
+            int64_t U = 0;
+            for (int c2 = 0; c2 < D; ++c2) num[c2] = 0;
+            for (int j = 0; j < nj; ++j) {
+                float dlt = fmaf((float)S[j], c, -mnew);
+                float x = rintf(dlt);
+                u[j] = pmap_u(x, tau);
+                U += u[j];
+                const int8_t *vj = vc + (size_t)(j0 + j) * D;
+                for (int c2 = 0; c2 < D; ++c2) num[c2] += (int64_t)u[j] * vj[c2];
+            }
+            double beta = exp2(((double)m - (double)mnew) / (double)ORA_PGRID);
+            for (int c2 = 0; c2 < D; ++c2) A[c2] = A[c2] * beta + (double)num[c2];
+            L = L * beta + (double)U;
+            m = mnew;
+
+            if (kb == dbg_kb) {
+                for (int j = 0; j < ORA_BLOCK; ++j) {
+                    if (s_int) s_int[(size_t)r * ORA_BLOCK + j] = j < nj ? S[j] : 0;
+                    if (p_code) p_code[(size_t)r * ORA_BLOCK + j] =
+                        (int8_t)(j < nj ? u[j] - 8 : -8);
+                }
+                if (pv_int)
+                    for (int c2 = 0; c2 < D; ++c2) {
+                        int64_t acc = 0;
+                        for (int j = 0; j < nj; ++j)
+                            acc += (int64_t)(u[j] - 8) * vc[(size_t)(j0 + j) * D + c2];
+                        pv_int[(size_t)r * D + c2] = (int32_t)acc;
+                    }
+                if (m_after) m_after[r] = m;
+            }
+        }
+        for (int c2 = 0; c2 < D; ++c2)
+            o[(size_t)r * D + c2] = A[c2] * (double)sv[c2] / L;
+        if (m_out) m_out[r] = m;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Mixed-precision schedule ([RA] Sec. 5.1: FP16 on the first/last sampling
+ * steps and the first/last DiT blocks, INT4 elsewhere).  Reading: a call runs
+ * at full precision when its step OR its block is in a head/tail set.
+ * Returns 1 for the full-precision path, 0 for INT4.                       */
+int ora_schedule_full_precision(int steps_head, int steps_tail,
+                                int blocks_head, int blocks_tail,
+                                int step, int n_steps, int block, int n_blocks)
+{
+    int step_fp = step < steps_head || step >= n_steps - steps_tail;
+    int block_fp = block < blocks_head || block >= n_blocks - blocks_tail;
+    return step_fp || block_fp;
+}
