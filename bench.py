@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the RotateAttention INT4 attention forward on one MI355X.
+
+One step = one ra_attn_fwd call (RoPE + rotation + INT4 quantization prologue,
+then the INT4 FlashAttention kernel) over the Wan-like 720p workload
+(B1, H40, D128, grid 21x45x80 = 75,600 tokens, Half rotation) with seeded
+synthetic bf16 inputs already resident in HBM.  Prints one JSON line with
+effective TOPS (4 N^2 D H / t), the fraction of the INT8 MFMA peak, the bf16
+fallback kernel on the same inputs, the dominant kernel's roofline and the CPU
+oracle's throughput on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan720]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+KERNEL_SOURCE = os.path.join(ROOT, "bit_quantized_attention_rope3d_amd", "csrc", "ra_int4_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_int4_flash_fwd_wan720.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan720")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--main-only-steps", type=int, default=0,
+                    help="extra launches of the attention kernel alone (profiling)")
+    return ap.parse_args()
+
+
+def kernel_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_steps(fn, steps, stream):
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        fn(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    first, mid, last = [], [], []
+    for a, b, c in evs:
+        first.append(a.elapsed_time(b))
+        mid.append(b.elapsed_time(c))
+    total = evs[0][0].elapsed_time(evs[-1][2])
+    return total, first, mid, wall
+
+
+def cpu_baseline(w, q, k, v, gpu_out, target_s):
+    """The oracle as it stands, on one head at full N: its prologue for that
+    head plus the attention of a block of query rows, scaled to effective
+    TOPS.  Also compares those rows with the GPU output."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    threads = oracle.get_threads()
+    h = 0
+    qs = np.ascontiguousarray(q[:, :, h:h + 1, :])
+    ks = np.ascontiguousarray(k[:, :, h:h + 1, :])
+    vs = np.ascontiguousarray(v[:, :, h:h + 1, :])
+    t0 = time.perf_counter()
+    pro = oracle.prologue(qs, ks, vs, w.grid, w.seg, w.theta, w.rot_id)
+    t_pro = time.perf_counter() - t0
+    N, D = w.tokens, w.head_dim
+    probe = np.arange(N - 64 * threads, N, dtype=np.int32)[-min(N, 64):]
+    t0 = time.perf_counter()
+    oracle.attention_rows(pro, 0, 0, probe)
+    t_probe = time.perf_counter() - t0
+    per_row = t_probe / probe.size
+    nrows = int(max(64, min(N, (target_s - t_pro) / max(per_row, 1e-9))))
+    nrows = (nrows // 64) * 64 or 64
+    rng = np.random.default_rng(7)
+    start = int(rng.integers(0, max(1, N - nrows)))
+    rows = np.arange(start, start + nrows, dtype=np.int32)
+    rows = rows[rows < N]
+    t0 = time.perf_counter()
+    o = oracle.attention_rows(pro, 0, 0, rows)
+    t_att = time.perf_counter() - t0
+    ops = 4.0 * rows.size * N * D
+    got = gpu_out[0, rows, h, :].astype(np.float64)
+    diff = float(np.abs(got - o).max())
+    cos = float((got * o).sum() / np.sqrt((got * got).sum() * (o * o).sum()))
+    return dict(
+        value=ops / t_att / 1e12, unit="TOPS", cores=threads, kind="oracle",
+        sample="head 0 of %d at full N=%d: prologue of that head (%.1f s) + attention rows %d..%d "
+               "(%d rows, %.1f s); value = 4*rows*N*D / attention time"
+               % (w.heads, N, t_pro, int(rows[0]), int(rows[-1]), rows.size, t_att),
+        seconds=t_pro + t_att,
+        parity_rows=dict(rows=int(rows.size), max_abs_vs_gpu=diff, cosine_vs_gpu=cos))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the attention shards by head with no "
+              "collective; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from bit_quantized_attention_rope3d_amd import inputs
+    from bit_quantized_attention_rope3d_amd.api import Plan
+
+    w = inputs.get(args.workload)
+    log("generating %s inputs (seed %d)" % (w.name, w.seed))
+    q, k, v, info = inputs.generate(w)
+
+    def dev(x):
+        return torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    stream = torch.cuda.current_stream()
+    p4 = Plan(w.batch, w.heads, w.head_dim, w.grid, w.seg, rot=w.rot, prec="int4",
+              in_dtype="bf16", out_dtype="f32", rope_theta=w.theta)
+    ws4 = p4.workspace()
+    out4 = p4.empty_out()
+
+    def step4(e):
+        e[0].record(stream)
+        p4.prologue(qd, kd, vd, ws4, stream)
+        e[1].record(stream)
+        p4.main(out4, ws4, stream)
+        e[2].record(stream)
+
+    log("warmup int4 x%d" % args.warmup)
+    for _ in range(args.warmup):
+        p4.forward(qd, kd, vd, out=out4, workspace=ws4)
+    torch.cuda.synchronize()
+    log("timing int4 x%d" % args.steps)
+    total4, pro_ms, main_ms, wall4 = time_steps(step4, args.steps, stream)
+    ms4 = total4 / args.steps
+    for _ in range(args.main_only_steps):
+        p4.main(out4, ws4, stream)
+    torch.cuda.synchronize()
+
+    ops = w.ops()
+    tops = ops / (ms4 * 1e-3) / 1e12
+    main_avg = float(np.mean(main_ms))
+    pro_avg = float(np.mean(pro_ms))
+    achieved_main = ops / (main_avg * 1e-3) / 1e12
+
+    res_bf16 = None
+    if not args.no_bf16:
+        pb = Plan(w.batch, w.heads, w.head_dim, w.grid, w.seg, rot=w.rot, prec="bf16",
+                  in_dtype="bf16", out_dtype="f32", rope_theta=w.theta)
+        wsb = pb.workspace()
+        outb = pb.empty_out()
+
+        def stepb(e):
+            e[0].record(stream)
+            pb.prologue(qd, kd, vd, wsb, stream)
+            e[1].record(stream)
+            pb.main(outb, wsb, stream)
+            e[2].record(stream)
+
+        log("warmup bf16 x%d" % args.warmup)
+        for _ in range(args.warmup):
+            pb.forward(qd, kd, vd, out=outb, workspace=wsb)
+        torch.cuda.synchronize()
+        log("timing bf16 x%d" % args.steps)
+        totalb, prob, mainb, _ = time_steps(stepb, args.steps, stream)
+        msb = totalb / args.steps
+        res_bf16 = dict(ms_per_step=msb, main_ms=float(np.mean(mainb)), prologue_ms=float(np.mean(prob)),
+                        effective_tflops=ops / (msb * 1e-3) / 1e12,
+                        main_pct_bf16_peak=100.0 * ops / (float(np.mean(mainb)) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
+        del wsb, outb
+        pb.close()
+
+    # Prologue: algorithmic bytes (bf16 Q, K, V read once; packed Q, K, V written).
+    E = w.batch * w.tokens * w.heads * w.head_dim
+    pro_bytes = 3 * E * 2 + 3 * E // 2
+    traffic = traffic_for_current_kernel()
+    roof = dict(bound="mfma", achieved=achieved_main, peak=INT8_PEAK_TOPS, unit="TFLOP/s",
+                frac=achieved_main / INT8_PEAK_TOPS, traffic=traffic,
+                kernel="int4_flash_fwd (k_int4_attn<128>)", avg_launch_ms=main_avg,
+                ops_per_launch=ops, note="integer multiply-adds counted as 2 ops (TOP/s); "
+                "peak = MI355X dense INT8 MFMA 5.0 POP/s")
+
+    result = {
+        "metric": "INT4 attention fwd effective TOPS & % INT8 MFMA peak; speedup vs bf16 flash",
+        "value": tops,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms4,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "grid": list(w.grid), "tokens": w.tokens, "seg": list(w.seg), "rot": w.rot,
+                   "in_dtype": "bf16", "out_dtype": "f32", "seed": w.seed},
+        "pct_int8_peak": 100.0 * tops / INT8_PEAK_TOPS,
+        "int4_main_ms": main_avg,
+        "int4_prologue_ms": pro_avg,
+        "prologue_gbs": pro_bytes / (pro_avg * 1e-3) / 1e9,
+        "bf16_fallback": res_bf16,
+        "speedup_vs_bf16": (res_bf16["ms_per_step"] / ms4) if res_bf16 else None,
+        "wall_s_timed_int4": wall4,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
+        o = out4.cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, o, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+"""Torch-facing wrapper of libra_attn.so.
+
+PyTorch supplies device memory (tensors) and the stream; every step of the
+attention runs in the library's HIP kernels.  Nothing here computes the method.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import native
+from .native import check, lib
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _stream_ptr(stream=None, device=None):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Plan:
+    """A validated problem (shape + options) with its RoPE tables.
+
+    q, k, v, out are [B, N, H, D] contiguous CUDA tensors, N = F*H*W tokens in
+    (f, h, w) order.  rot: 'none' | 'interleaved' | 'half'; prec: 'int4' |
+    'bf16'; in_dtype/out_dtype: 'bf16' | 'f32'.
+    """
+
+    def __init__(self, batch, heads, head_dim, grid, seg, rot="half", prec="int4",
+                 in_dtype="bf16", out_dtype="f32", rope_theta=10000.0, softmax_scale=0.0,
+                 p_mode=0):
+        self.batch, self.heads, self.head_dim = int(batch), int(heads), int(head_dim)
+        self.grid = tuple(int(x) for x in grid)
+        self.seg = tuple(int(x) for x in seg)
+        self.rot, self.prec, self.in_dtype, self.out_dtype = rot, prec, in_dtype, out_dtype
+        self.tokens = self.grid[0] * self.grid[1] * self.grid[2]
+        self._shape = native.make_shape(self.batch, self.heads, self.head_dim, self.grid, self.seg)
+        self._opts = native.make_opts(rot, prec, in_dtype, out_dtype, rope_theta, softmax_scale,
+                                      p_mode)
+        h = ctypes.c_void_p()
+        check(lib().ra_plan_create(ctypes.byref(self._shape), ctypes.byref(self._opts),
+                                   ctypes.byref(h)), "ra_plan_create")
+        self._h = h
+        n = ctypes.c_size_t()
+        check(lib().ra_plan_workspace_size(self._h, ctypes.byref(n)), "ra_plan_workspace_size")
+        self.workspace_bytes = n.value
+
+    # -- lifetime -----------------------------------------------------------
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().ra_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- buffers ------------------------------------------------------------
+    @property
+    def io_shape(self):
+        return (self.batch, self.tokens, self.heads, self.head_dim)
+
+    def workspace(self, device="cuda"):
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device)
+
+    def empty_out(self, device="cuda"):
+        return torch.empty(self.io_shape, dtype=_TORCH_DT[self.out_dtype], device=device)
+
+    def _check_in(self, *ts):
+        want = _TORCH_DT[self.in_dtype]
+        for t in ts:
+            if tuple(t.shape) != self.io_shape or t.dtype != want or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError("input must be a contiguous CUDA %s tensor of shape %s (got %s %s)"
+                                 % (want, self.io_shape, t.dtype, tuple(t.shape)))
+
+    def _ws(self, workspace, device):
+        if workspace is None:
+            workspace = self.workspace(device)
+        return workspace
+
+    # -- calls --------------------------------------------------------------
+    def forward(self, q, k, v, out=None, workspace=None, stream=None):
+        self._check_in(q, k, v)
+        out = self.empty_out(q.device) if out is None else out
+        ws = self._ws(workspace, q.device)
+        check(lib().ra_attn_fwd(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
+                                ws.numel(), _stream_ptr(stream, q.device)), "ra_attn_fwd")
+        return out
+
+    __call__ = forward
+
+    def prologue(self, q, k, v, workspace, stream=None):
+        self._check_in(q, k, v)
+        check(lib().ra_attn_prologue(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(workspace),
+                                     workspace.numel(), _stream_ptr(stream, q.device)),
+              "ra_attn_prologue")
+
+    def main(self, out, workspace, stream=None):
+        check(lib().ra_attn_main(self._h, _ptr(out), _ptr(workspace), workspace.numel(),
+                                 _stream_ptr(stream, out.device)), "ra_attn_main")
+        return out
+
+    # -- parity exports -----------------------------------------------------
+    def debug_prologue(self, q, k, v, workspace=None):
+        self._check_in(q, k, v)
+        ws = self._ws(workspace, q.device)
+        B, N, H, D = self.io_shape
+        nblk = (N + 63) // 64
+        qc = np.empty((B, H, N, D), np.int8)
+        kc = np.empty((B, H, N, D), np.int8)
+        vc = np.empty((B, H, N, D), np.int8)
+        sq = np.empty((B, H, nblk), np.float32)
+        sk = np.empty((B, H, nblk), np.float32)
+        sv = np.empty((B, H, D), np.float32)
+        P = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        check(lib().ra_debug_prologue(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel(),
+                                      P(qc), P(sq), P(kc), P(sk), P(vc), P(sv),
+                                      _stream_ptr(None, q.device)), "ra_debug_prologue")
+        return dict(q_codes=qc, s_q=sq, k_codes=kc, s_k=sk, v_codes=vc, s_v=sv)
+
+    def debug_tile(self, workspace, b, h, q_blk, kv_blk):
+        D = self.head_dim
+        s_int = np.empty((64, 64), np.int32)
+        p_code = np.empty((64, 64), np.int8)
+        pv = np.empty((64, D), np.int32)
+        m = np.empty(64, np.float32)
+        P = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        check(lib().ra_debug_tile(self._h, _ptr(workspace), workspace.numel(), b, h, q_blk, kv_blk,
+                                  P(s_int), P(p_code), P(pv), P(m),
+                                  _stream_ptr(None, workspace.device)), "ra_debug_tile")
+        return dict(s_int=s_int, p_code=p_code, pv_int=pv, m_after=m)
+
+    def tables(self, seg: int):
+        npos = self.grid[seg]
+        half = self.seg[seg] // 2
+        cs = np.empty((npos, half), np.float32)
+        sn = np.empty((npos, half), np.float32)
+        check(lib().ra_debug_tables(self._h, seg, cs.ctypes.data_as(ctypes.c_void_p),
+                                    sn.ctypes.data_as(ctypes.c_void_p)), "ra_debug_tables")
+        return cs, sn
+
+
+def attn_fwd(q, k, v, grid, seg, rot="half", prec="int4", out_dtype="f32", workspace=None,
+             stream=None):
+    """One-shot forward through ra_attn_fwd_simple (plans cached in the library)."""
+    B, N, H, D = q.shape
+    in_dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}[q.dtype]
+    shape = native.make_shape(B, H, D, grid, seg)
+    opts = native.make_opts(rot, prec, in_dtype, out_dtype)
+    n = ctypes.c_size_t()
+    check(lib().ra_workspace_size(ctypes.byref(shape), ctypes.byref(opts), ctypes.byref(n)),
+          "ra_workspace_size")
+    ws = workspace if workspace is not None else torch.empty(n.value, dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, N, H, D), dtype=_TORCH_DT[out_dtype], device=q.device)
+    check(lib().ra_attn_fwd_simple(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, D, *grid, *seg,
+                                   native.ROT[rot], native.PREC[prec], native.DT[in_dtype],
+                                   native.DT[out_dtype], _ptr(ws), ws.numel(),
+                                   _stream_ptr(stream, q.device)), "ra_attn_fwd_simple")
+    return out
+
+
+def schedule_pick(sched, step, n_steps, block, n_blocks) -> str:
+    """'bf16' on the head/tail steps or blocks of `sched` = (steps_head,
+    steps_tail, blocks_head, blocks_tail), else 'int4'."""
+    s = native.RaSchedule(*[int(x) for x in sched])
+    return "bf16" if lib().ra_schedule_pick(ctypes.byref(s), step, n_steps, block, n_blocks) else "int4"
+
+
+def pmap_device(x: torch.Tensor) -> torch.Tensor:
+    """The kernels' P map on grid exponents x (float32 CUDA tensor) -> u = code + 8."""
+    x = x.contiguous()
+    u = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    check(lib().ra_debug_pmap(_ptr(x), _ptr(u), x.numel(), _stream_ptr(None, x.device)),
+          "ra_debug_pmap")
+    return u
+
+
+def copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int | None = None, stream=None):
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    check(lib().ra_copy(_ptr(dst), _ptr(src), nbytes, _stream_ptr(stream, src.device)), "ra_copy")
+
+
+def pgrid() -> int:
+    return int(lib().ra_pgrid())

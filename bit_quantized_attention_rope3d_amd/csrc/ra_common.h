@@ -1,0 +1,116 @@
+// ra_common.h -- device-side building blocks shared by the RotateAttention
+// kernels for gfx950 (CDNA4).  Internal to libra_attn.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned short v8u16 __attribute__((ext_vector_type(8)));
+
+constexpr int kBlock = 64;          // tokens per Q/K scale block and per key step
+constexpr int kWave = 64;
+
+// Exponent grid of the range-optimized P map: the exponent of p (in log2
+// units) is rounded to a multiple of 1/kPGrid.  On this grid no point other
+// than p = 1/2 comes within 3e-5 (relative) of a rounding boundary of 15 p,
+// so the hardware exp2 (error ~1e-7) decides every code exactly; an
+// exhaustive probe over all grid points checks it.
+constexpr int kPGrid = 4755;
+constexpr float kInvPGrid = 1.0f / 4755.0f;
+constexpr float kLog2Of15 = (float)3.9068905956085187;
+
+// Packed INT4 layout, shared by the prologue (writer) and the attention
+// kernels (readers):
+//   * Q/K rows: D/2 bytes per token; 16-channel group g occupies bytes
+//     8g..8g+7, byte i of a group holds channel 16g+i in its high nibble and
+//     channel 16g+i+8 in its low nibble (two's-complement nibbles).
+//   * V tile of one 64-key block: for each channel d, 32 bytes holding the 64
+//     key slots in MFMA operand order, grouped by 16 slots like Q/K rows.
+//   Slot s = 32*ks + 16*hf + j carries key 32*ks + 8*(j/4) + 4*hf + (j%4):
+//   the key that the 32x32 MFMA accumulator of S^T = K Q^T leaves in
+//   register j of the lane half hf, so P feeds the PV MFMA with no shuffle.
+__host__ __device__ constexpr int slot_key_i8(int slot) {
+  return 32 * (slot >> 5) + 8 * ((slot & 15) >> 2) + 4 * ((slot >> 4) & 1) + (slot & 3);
+}
+
+// bf16 path: 16-slot K-steps; slot s = 16*ks + 8*hf + j carries key
+// 32*(ks/2) + 8*(2*(ks%2) + j/4) + 4*hf + (j%4).
+__host__ __device__ constexpr int slot_key_bf16(int slot) {
+  return 32 * (slot >> 5) + 8 * (2 * ((slot >> 4) & 1) + ((slot & 7) >> 2)) +
+         4 * ((slot >> 3) & 1) + (slot & 3);
+}
+
+// Widen 8 packed nibble codes (one dword) to 16*code int8 values:
+// high nibbles -> bytes of `hi`, low nibbles -> bytes of `lo`.
+__device__ __forceinline__ void unpack_x16(uint32_t w, uint32_t& hi, uint32_t& lo) {
+  hi = w & 0xF0F0F0F0u;
+  lo = (w << 4) & 0xF0F0F0F0u;
+}
+
+// Range-optimized P code, as u = code + 8 in [0, 15], of the grid exponent
+// x (an integer-valued float <= 0), written into byte `sel` of `acc`.
+__device__ __forceinline__ uint32_t pmap_insert(float x, uint32_t sel, uint32_t acc) {
+  float w = __builtin_fmaf(x, kInvPGrid, kLog2Of15);
+  float y = __builtin_amdgcn_exp2f(w);
+  return __builtin_amdgcn_cvt_pk_u8_f32(y, sel, acc);
+}
+
+// Smallest float >= the exact product s * c (c finite, s an integer-valued
+// float with |s| < 2^24).
+__device__ __forceinline__ float mul_round_up(float s, float c) {
+  float m = s * c;
+  float r = __builtin_fmaf(s, c, -m);
+  if (r > 0.0f) {
+    uint32_t b = __float_as_uint(m);
+    b = (m > 0.0f) ? b + 1u : (m < 0.0f ? b - 1u : 1u);
+    m = __uint_as_float(b);
+  }
+  return m;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Combine the values of lanes l and l^32 (the two halves of a wave hold the
+// same query columns).  v_permlane32_swap returns, per lane, its own value in
+// one result and its partner's in the other, so a symmetric op of both
+// results is the cross-half reduction whichever half the lane is in.
+__device__ __forceinline__ int xhalf_max_i(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ float xhalf_max_f(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum_f(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+// Segment tables for 3D RoPE: cos/sin of segment s at [pos * (seg[s]/2) + pair].
+struct RopeTabs {
+  const float* cs[3];
+  const float* sn[3];
+  int seg[3];
+  int off[3];
+  int dims[3];   // F, H, W
+};
+
+}  // namespace ra

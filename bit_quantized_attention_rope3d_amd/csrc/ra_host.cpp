@@ -1,0 +1,566 @@
+// ra_host.cpp -- host runtime behind include/ra_attn.h: validation, plans,
+// RoPE tables, workspace layout, launches, error reporting, the step/block
+// schedule and the parity exports.
+//
+// Method source: "RotateAttention: RoPE-Aware Rotation and Range Rectification
+// for INT4 Quantized Attention in Video Generation" (pith.science review):
+// Sec. 3 / Fig. 2 (3D RoPE segments), Sec. 4.1 / Fig. 3 (Interleaved rotation
+// merged into RoPE), Sec. 4.2 (P map), Sec. 5.1 (FP16 step/block fallback).
+#include "ra_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "ra_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ra_status fail(ra_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+ra_status ok() {
+  g_err.clear();
+  return RA_OK;
+}
+
+// RA_FAULT_INJECT=alloc|launch forces the matching failure path (host-side
+// tests of error mapping).
+bool inject(const char* what) {
+  const char* e = std::getenv("RA_FAULT_INJECT");
+  return e && std::strcmp(e, what) == 0;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  int N, Npad, nblk, nkb, nqt;
+  size_t off_q, off_k, off_v, off_sq, off_sk, off_sv, off_vamax, off_dbg, total;
+};
+
+constexpr size_t kDbgBytes(int D) { return 64 * 64 * 4 + 64 * 64 + (size_t)64 * D * 4 + 64 * 4 + 1024; }
+
+ra_status validate(const ra_shape* s, const ra_opts* o) {
+  if (!s || !o) return fail(RA_ERR_INVALID_ARG, "shape and opts must be non-null");
+  if (s->batch < 1 || s->heads < 1 || s->grid_f < 1 || s->grid_h < 1 || s->grid_w < 1)
+    return fail(RA_ERR_SHAPE, "batch, heads and grid dims must be >= 1 (got B=%d H=%d grid=%dx%dx%d)",
+                s->batch, s->heads, s->grid_f, s->grid_h, s->grid_w);
+  const long long N = (long long)s->grid_f * s->grid_h * s->grid_w;
+  if (N > (1LL << 26))
+    return fail(RA_ERR_SHAPE, "token count %lld exceeds the supported 2^26", N);
+  if ((long long)s->batch * s->heads * ((N + 255) / 256) > 0x7FFFFFFFLL)
+    return fail(RA_ERR_SHAPE, "batch * heads * ceil(N/256) does not fit a launch grid");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", s->head_dim);
+  for (int i = 0; i < 3; ++i)
+    if (s->seg[i] < 2 || (s->seg[i] & 1))
+      return fail(RA_ERR_SEGMENTS, "segment %d has length %d; RoPE segments must be even and >= 2",
+                  i, s->seg[i]);
+  if (s->seg[0] + s->seg[1] + s->seg[2] != s->head_dim)
+    return fail(RA_ERR_SEGMENTS, "segments %d+%d+%d do not sum to head_dim %d", s->seg[0], s->seg[1],
+                s->seg[2], s->head_dim);
+  if (o->rot < RA_ROT_NONE || o->rot > RA_ROT_HALF)
+    return fail(RA_ERR_INVALID_ARG, "rot %d is not a ra_rot", o->rot);
+  if (o->prec != RA_PREC_INT4 && o->prec != RA_PREC_BF16)
+    return fail(RA_ERR_INVALID_ARG, "prec %d is not a ra_prec", o->prec);
+  if ((o->in_dtype != RA_DT_F32 && o->in_dtype != RA_DT_BF16) ||
+      (o->out_dtype != RA_DT_F32 && o->out_dtype != RA_DT_BF16))
+    return fail(RA_ERR_DTYPE, "dtypes must be RA_DT_F32 or RA_DT_BF16 (in=%d out=%d)", o->in_dtype,
+                o->out_dtype);
+  if (!(o->rope_theta > 0.0) || !std::isfinite(o->rope_theta))
+    return fail(RA_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (!(o->softmax_scale >= 0.0) || !std::isfinite(o->softmax_scale))
+    return fail(RA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (o->p_mode != 0)
+    return fail(RA_ERR_UNSUPPORTED, "p_mode %d not implemented (0 = range-optimized)", o->p_mode);
+  return RA_OK;
+}
+
+Layout layout_of(const ra_shape* s, const ra_opts* o) {
+  Layout L{};
+  L.N = s->grid_f * s->grid_h * s->grid_w;
+  L.nblk = (L.N + ra::kBlock - 1) / ra::kBlock;
+  L.nkb = L.nblk;
+  L.Npad = L.nblk * ra::kBlock;
+  L.nqt = (L.N + 255) / 256;
+  const size_t BH = (size_t)s->batch * s->heads, D = s->head_dim;
+  const size_t A = 256;
+  size_t off = 0;
+  if (o->prec == RA_PREC_INT4) {
+    const size_t tens = BH * L.Npad * D / 2;
+    L.off_q = off; off = align_up(off + tens, A);
+    L.off_k = off; off = align_up(off + tens, A);
+    L.off_v = off; off = align_up(off + tens, A);
+    L.off_sq = off; off = align_up(off + BH * L.nblk * 4, A);
+    L.off_sk = off; off = align_up(off + BH * L.nblk * 4, A);
+    L.off_sv = off; off = align_up(off + BH * D * 4, A);
+    L.off_vamax = off; off = align_up(off + BH * D * 4, A);
+    L.off_dbg = off; off = align_up(off + kDbgBytes((int)D), A);
+  } else {
+    const size_t tens = BH * L.Npad * D * 2;
+    L.off_q = off; off = align_up(off + tens, A);
+    L.off_k = off; off = align_up(off + tens, A);
+    L.off_v = off; off = align_up(off + tens, A);
+    L.off_sq = L.off_sk = L.off_sv = L.off_vamax = L.off_dbg = off;
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct ra_plan_s {
+  ra_shape shape;
+  ra_opts opts;
+  Layout lay;
+  int off[3];
+  std::vector<float> cs[3], sn[3];
+  size_t tab_floats;
+  float alpha_g, alpha;
+  std::mutex mu;
+  std::map<int, float*> dev_tabs;
+};
+
+namespace {
+
+// cos/sin of pos * theta^(-2j/L) (+ pi/4 when the Interleaved rotation is
+// merged), angles in binary64, each value rounded once to binary32.
+void build_tables(ra_plan_s* p) {
+  const int dims[3] = {p->shape.grid_f, p->shape.grid_h, p->shape.grid_w};
+  const bool merged = p->opts.prec == RA_PREC_INT4 && p->opts.rot == RA_ROT_INTERLEAVED;
+  p->tab_floats = 0;
+  int off = 0;
+  for (int s = 0; s < 3; ++s) {
+    const int L = p->shape.seg[s], half = L / 2;
+    p->off[s] = off;
+    off += L;
+    p->cs[s].resize((size_t)dims[s] * half);
+    p->sn[s].resize((size_t)dims[s] * half);
+    for (int pos = 0; pos < dims[s]; ++pos)
+      for (int j = 0; j < half; ++j) {
+        const double e = (double)(-2 * j) / (double)L;
+        const double freq = std::pow(p->opts.rope_theta, e);
+        double ang = (double)pos * freq;
+        if (merged) {
+          const double quarter = M_PI / 4.0;
+          ang = ang + quarter;
+        }
+        p->cs[s][(size_t)pos * half + j] = (float)std::cos(ang);
+        p->sn[s][(size_t)pos * half + j] = (float)std::sin(ang);
+      }
+    p->tab_floats += 2 * p->cs[s].size();
+  }
+}
+
+ra_status device_tables(ra_plan p, ra::RopeTabs* t) {
+  if (inject("alloc")) return fail(RA_ERR_OOM, "injected allocation failure (RA_FAULT_INJECT=alloc)");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(RA_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> g(p->mu);
+  auto it = p->dev_tabs.find(dev);
+  float* buf = nullptr;
+  if (it == p->dev_tabs.end()) {
+    if (hipMalloc(&buf, p->tab_floats * sizeof(float)) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(RA_ERR_OOM, "hipMalloc of %zu bytes of RoPE tables failed", p->tab_floats * sizeof(float));
+    }
+    std::vector<float> host;
+    host.reserve(p->tab_floats);
+    for (int s = 0; s < 3; ++s) {
+      host.insert(host.end(), p->cs[s].begin(), p->cs[s].end());
+      host.insert(host.end(), p->sn[s].begin(), p->sn[s].end());
+    }
+    if (hipMemcpy(buf, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+      hipFree(buf);
+      return fail(RA_ERR_HIP, "copying RoPE tables to device %d failed", dev);
+    }
+    p->dev_tabs[dev] = buf;
+  } else {
+    buf = it->second;
+  }
+  const int dims[3] = {p->shape.grid_f, p->shape.grid_h, p->shape.grid_w};
+  size_t o = 0;
+  for (int s = 0; s < 3; ++s) {
+    t->cs[s] = buf + o;
+    o += p->cs[s].size();
+    t->sn[s] = buf + o;
+    o += p->sn[s].size();
+    t->seg[s] = p->shape.seg[s];
+    t->off[s] = p->off[s];
+    t->dims[s] = dims[s];
+  }
+  return RA_OK;
+}
+
+bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+ra_status check_ws(ra_plan p, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(RA_ERR_WORKSPACE, "workspace is null");
+  if (misaligned(ws)) return fail(RA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  if (ws_bytes < p->lay.total)
+    return fail(RA_ERR_WORKSPACE, "workspace has %zu bytes; this plan needs %zu", ws_bytes, p->lay.total);
+  return RA_OK;
+}
+
+ra_status after_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return RA_OK;
+}
+
+ra::AttnArgs attn_args(ra_plan p, uint8_t* ws, void* o) {
+  ra::AttnArgs a{};
+  a.qp = ws + p->lay.off_q;
+  a.kp = ws + p->lay.off_k;
+  a.vp = ws + p->lay.off_v;
+  a.s_q = reinterpret_cast<const float*>(ws + p->lay.off_sq);
+  a.s_k = reinterpret_cast<const float*>(ws + p->lay.off_sk);
+  a.s_v = reinterpret_cast<const float*>(ws + p->lay.off_sv);
+  a.out = o;
+  a.N = p->lay.N;
+  a.H = p->shape.heads;
+  a.Npad = p->lay.Npad;
+  a.nblk = p->lay.nblk;
+  a.nkb = p->lay.nkb;
+  a.nqt = p->lay.nqt;
+  a.alpha_g = p->alpha_g;
+  a.alpha = p->alpha;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_opts_default(ra_opts* o) {
+  if (!o) return fail(RA_ERR_INVALID_ARG, "opts is null");
+  std::memset(o, 0, sizeof *o);
+  o->rot = RA_ROT_HALF;
+  o->prec = RA_PREC_INT4;
+  o->in_dtype = RA_DT_BF16;
+  o->out_dtype = RA_DT_F32;
+  o->rope_theta = 10000.0;
+  o->softmax_scale = 0.0;
+  o->p_mode = 0;
+  return ok();
+}
+
+ra_status ra_plan_create(const ra_shape* shape, const ra_opts* opts, ra_plan* out) {
+  if (!out) return fail(RA_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  ra_status st = validate(shape, opts);
+  if (st != RA_OK) return st;
+  ra_plan p = new (std::nothrow) ra_plan_s();
+  if (!p) return fail(RA_ERR_OOM, "host allocation of the plan failed");
+  p->shape = *shape;
+  p->opts = *opts;
+  p->lay = layout_of(shape, opts);
+  const double scale = opts->softmax_scale > 0.0 ? opts->softmax_scale : 1.0 / std::sqrt((double)shape->head_dim);
+  p->alpha_g = (float)(M_LOG2E * scale * (double)ra::kPGrid);
+  p->alpha = (float)(M_LOG2E * scale);
+  build_tables(p);
+  *out = p;
+  return ok();
+}
+
+ra_status ra_plan_destroy(ra_plan p) {
+  if (!p) return ok();
+  for (auto& kv : p->dev_tabs) {
+    int cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first) == hipSuccess) {
+      hipFree(kv.second);
+      hipSetDevice(cur);
+    }
+  }
+  delete p;
+  return ok();
+}
+
+ra_status ra_plan_workspace_size(ra_plan p, size_t* bytes) {
+  if (!p || !bytes) return fail(RA_ERR_INVALID_ARG, "plan and bytes must be non-null");
+  *bytes = p->lay.total;
+  return ok();
+}
+
+ra_status ra_workspace_size(const ra_shape* shape, const ra_opts* opts, size_t* bytes) {
+  if (!bytes) return fail(RA_ERR_INVALID_ARG, "bytes is null");
+  ra_status st = validate(shape, opts);
+  if (st != RA_OK) return st;
+  *bytes = layout_of(shape, opts).total;
+  return ok();
+}
+
+ra_status ra_attn_prologue(ra_plan p, const void* q, const void* k, const void* v, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!p) return fail(RA_ERR_INVALID_ARG, "plan is null");
+  if (!q || !k || !v) return fail(RA_ERR_INVALID_ARG, "q, k and v must be non-null");
+  if (misaligned(q) || misaligned(k) || misaligned(v))
+    return fail(RA_ERR_ALIGNMENT, "q, k and v must be 16-byte aligned");
+  ra_status st = check_ws(p, ws, ws_bytes);
+  if (st != RA_OK) return st;
+  if (inject("launch")) return fail(RA_ERR_HIP, "injected launch failure (RA_FAULT_INJECT=launch)");
+  ra::RopeTabs tabs;
+  st = device_tables(p, &tabs);
+  if (st != RA_OK) return st;
+
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const int D = p->shape.head_dim;
+  const bool in_bf16 = p->opts.in_dtype == RA_DT_BF16;
+  ra::QKPrologueArgs qa{};
+  qa.q = q;
+  qa.k = k;
+  qa.q_out = w + p->lay.off_q;
+  qa.k_out = w + p->lay.off_k;
+  qa.s_q = reinterpret_cast<float*>(w + p->lay.off_sq);
+  qa.s_k = reinterpret_cast<float*>(w + p->lay.off_sk);
+  qa.tabs = tabs;
+  qa.B = p->shape.batch;
+  qa.N = p->lay.N;
+  qa.H = p->shape.heads;
+  qa.Npad = p->lay.Npad;
+  qa.nblk = p->lay.nblk;
+  ra::VQuantArgs vq{};
+  vq.v = v;
+  vq.vamax = reinterpret_cast<const uint32_t*>(w + p->lay.off_vamax);
+  vq.v_out = w + p->lay.off_v;
+  vq.s_v = reinterpret_cast<float*>(w + p->lay.off_sv);
+  vq.N = p->lay.N;
+  vq.H = p->shape.heads;
+  vq.nkb = p->lay.nkb;
+  if (p->opts.prec == RA_PREC_INT4) {
+    ra::VAmaxArgs va{};
+    va.v = v;
+    va.vamax = reinterpret_cast<uint32_t*>(w + p->lay.off_vamax);
+    va.N = p->lay.N;
+    va.H = p->shape.heads;
+    va.chunk = 512;
+    ra::launch_int4_prologue(qa, va, vq, D, p->opts.rot, in_bf16, stream);
+  } else {
+    ra::launch_bf16_prologue(qa, vq, D, in_bf16, stream);
+  }
+  st = after_launch("prologue");
+  return st == RA_OK ? ok() : st;
+}
+
+ra_status ra_attn_main(ra_plan p, void* o, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!p) return fail(RA_ERR_INVALID_ARG, "plan is null");
+  if (!o) return fail(RA_ERR_INVALID_ARG, "o must be non-null");
+  if (misaligned(o)) return fail(RA_ERR_ALIGNMENT, "o must be 16-byte aligned");
+  ra_status st = check_ws(p, ws, ws_bytes);
+  if (st != RA_OK) return st;
+  if (inject("launch")) return fail(RA_ERR_HIP, "injected launch failure (RA_FAULT_INJECT=launch)");
+  ra::AttnArgs a = attn_args(p, static_cast<uint8_t*>(ws), o);
+  const bool out_bf16 = p->opts.out_dtype == RA_DT_BF16;
+  if (p->opts.prec == RA_PREC_INT4)
+    ra::launch_int4_attn(a, p->shape.head_dim, out_bf16, p->shape.batch, stream);
+  else
+    ra::launch_bf16_attn(a, p->shape.head_dim, out_bf16, p->shape.batch, stream);
+  st = after_launch("attention");
+  return st == RA_OK ? ok() : st;
+}
+
+ra_status ra_attn_fwd(ra_plan p, const void* q, const void* k, const void* v, void* o, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  if (!o) return fail(RA_ERR_INVALID_ARG, "o must be non-null");
+  if (misaligned(o)) return fail(RA_ERR_ALIGNMENT, "o must be 16-byte aligned");
+  ra_status st = ra_attn_prologue(p, q, k, v, ws, ws_bytes, stream);
+  if (st != RA_OK) return st;
+  return ra_attn_main(p, o, ws, ws_bytes, stream);
+}
+
+ra_status ra_attn_fwd_simple(const void* q, const void* k, const void* v, void* o, int32_t batch,
+                             int32_t heads, int32_t head_dim, int32_t grid_f, int32_t grid_h,
+                             int32_t grid_w, int32_t seg_f, int32_t seg_h, int32_t seg_w, int32_t rot,
+                             int32_t prec, int32_t in_dtype, int32_t out_dtype, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  static std::mutex mu;
+  static std::map<std::vector<int32_t>, ra_plan> cache;
+  ra_shape s{batch, heads, head_dim, grid_f, grid_h, grid_w, {seg_f, seg_h, seg_w}};
+  ra_opts op;
+  ra_opts_default(&op);
+  op.rot = rot;
+  op.prec = prec;
+  op.in_dtype = in_dtype;
+  op.out_dtype = out_dtype;
+  ra_status st = validate(&s, &op);
+  if (st != RA_OK) return st;
+  std::vector<int32_t> key{batch, heads, head_dim, grid_f, grid_h, grid_w, seg_f, seg_h, seg_w,
+                           rot, prec, in_dtype, out_dtype};
+  ra_plan p = nullptr;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      p = it->second;
+    } else {
+      st = ra_plan_create(&s, &op, &p);
+      if (st != RA_OK) return st;
+      cache[key] = p;
+    }
+  }
+  return ra_attn_fwd(p, q, k, v, o, ws, ws_bytes, stream);
+}
+
+ra_prec ra_schedule_pick(const ra_schedule* s, int32_t step, int32_t n_steps, int32_t block,
+                         int32_t n_blocks) {
+  if (!s) return RA_PREC_BF16;
+  const bool step_full = step < s->steps_head || step >= n_steps - s->steps_tail;
+  const bool block_full = block < s->blocks_head || block >= n_blocks - s->blocks_tail;
+  return (step_full || block_full) ? RA_PREC_BF16 : RA_PREC_INT4;
+}
+
+const char* ra_status_str(ra_status s) {
+  switch (s) {
+    case RA_OK: return "RA_OK";
+    case RA_ERR_INVALID_ARG: return "RA_ERR_INVALID_ARG";
+    case RA_ERR_SHAPE: return "RA_ERR_SHAPE";
+    case RA_ERR_SEGMENTS: return "RA_ERR_SEGMENTS";
+    case RA_ERR_DTYPE: return "RA_ERR_DTYPE";
+    case RA_ERR_ALIGNMENT: return "RA_ERR_ALIGNMENT";
+    case RA_ERR_WORKSPACE: return "RA_ERR_WORKSPACE";
+    case RA_ERR_UNSUPPORTED: return "RA_ERR_UNSUPPORTED";
+    case RA_ERR_OOM: return "RA_ERR_OOM";
+    case RA_ERR_HIP: return "RA_ERR_HIP";
+  }
+  return "RA_ERR_UNKNOWN";
+}
+
+const char* ra_last_error_message(void) { return g_err.c_str(); }
+
+int32_t ra_pgrid(void) { return ra::kPGrid; }
+
+ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void* v, void* ws,
+                            size_t ws_bytes, int8_t* q_codes, float* s_q, int8_t* k_codes,
+                            float* s_k, int8_t* v_codes, float* s_v, hipStream_t stream) {
+  if (!p) return fail(RA_ERR_INVALID_ARG, "plan is null");
+  if (p->opts.prec != RA_PREC_INT4) return fail(RA_ERR_UNSUPPORTED, "debug prologue needs an INT4 plan");
+  if (!q_codes || !s_q || !k_codes || !s_k || !v_codes || !s_v)
+    return fail(RA_ERR_INVALID_ARG, "host output buffers must be non-null");
+  ra_status st = ra_attn_prologue(p, q, k, v, ws, ws_bytes, stream);
+  if (st != RA_OK) return st;
+  if (hipStreamSynchronize(stream) != hipSuccess) return fail(RA_ERR_HIP, "prologue failed on device");
+  const Layout& L = p->lay;
+  const size_t BH = (size_t)p->shape.batch * p->shape.heads;
+  const int D = p->shape.head_dim, N = L.N;
+  const size_t tens = BH * L.Npad * D / 2;
+  std::vector<uint8_t> pq(tens), pk(tens), pv(tens);
+  const uint8_t* w = static_cast<const uint8_t*>(ws);
+  if (hipMemcpy(pq.data(), w + L.off_q, tens, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(pk.data(), w + L.off_k, tens, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(pv.data(), w + L.off_v, tens, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(s_q, w + L.off_sq, BH * L.nblk * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(s_k, w + L.off_sk, BH * L.nblk * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(s_v, w + L.off_sv, BH * D * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(RA_ERR_HIP, "copy of prologue outputs failed");
+  auto nib = [](uint8_t byte, bool high) -> int8_t {
+    int x = high ? (byte >> 4) : (byte & 15);
+    return (int8_t)(x >= 8 ? x - 16 : x);
+  };
+  // Q/K rows: group g of 16 channels, byte i -> channel 16g+i (high), 16g+i+8 (low).
+  for (size_t bh = 0; bh < BH; ++bh)
+    for (int n = 0; n < N; ++n) {
+      const uint8_t* rq = pq.data() + (bh * L.Npad + n) * (D / 2);
+      const uint8_t* rk = pk.data() + (bh * L.Npad + n) * (D / 2);
+      int8_t* oq = q_codes + (bh * N + n) * D;
+      int8_t* ok_ = k_codes + (bh * N + n) * D;
+      for (int g = 0; g < D / 16; ++g)
+        for (int i = 0; i < 8; ++i) {
+          oq[16 * g + i] = nib(rq[8 * g + i], true);
+          oq[16 * g + i + 8] = nib(rq[8 * g + i], false);
+          ok_[16 * g + i] = nib(rk[8 * g + i], true);
+          ok_[16 * g + i + 8] = nib(rk[8 * g + i], false);
+        }
+    }
+  // V: per 64-key block and channel, 64 slots in operand order.
+  for (size_t bh = 0; bh < BH; ++bh)
+    for (int kb = 0; kb < L.nkb; ++kb)
+      for (int d = 0; d < D; ++d) {
+        const uint8_t* r = pv.data() + ((bh * L.nkb + kb) * D + d) * 32;
+        for (int sg = 0; sg < 4; ++sg)
+          for (int i = 0; i < 8; ++i) {
+            const int key_hi = kb * 64 + ra::slot_key_i8(sg * 16 + i);
+            const int key_lo = kb * 64 + ra::slot_key_i8(sg * 16 + i + 8);
+            if (key_hi < N) v_codes[(bh * N + key_hi) * D + d] = nib(r[8 * sg + i], true);
+            if (key_lo < N) v_codes[(bh * N + key_lo) * D + d] = nib(r[8 * sg + i], false);
+          }
+      }
+  return ok();
+}
+
+ra_status ra_debug_tile(ra_plan p, void* ws, size_t ws_bytes, int32_t b, int32_t h, int32_t q_blk,
+                        int32_t kv_blk, int32_t* s_int, int8_t* p_codes, int32_t* pv_int,
+                        float* m_after, hipStream_t stream) {
+  if (!p) return fail(RA_ERR_INVALID_ARG, "plan is null");
+  if (p->opts.prec != RA_PREC_INT4) return fail(RA_ERR_UNSUPPORTED, "debug tile needs an INT4 plan");
+  if (!s_int || !p_codes || !pv_int || !m_after)
+    return fail(RA_ERR_INVALID_ARG, "host output buffers must be non-null");
+  if (b < 0 || b >= p->shape.batch || h < 0 || h >= p->shape.heads || q_blk < 0 ||
+      q_blk >= p->lay.nblk || kv_blk < 0 || kv_blk >= p->lay.nkb)
+    return fail(RA_ERR_INVALID_ARG, "tile index out of range");
+  ra_status st = check_ws(p, ws, ws_bytes);
+  if (st != RA_OK) return st;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const int D = p->shape.head_dim;
+  ra::AttnArgs a = attn_args(p, w, nullptr);
+  ra::TileDumpArgs t{};
+  uint8_t* dbg = w + p->lay.off_dbg;
+  t.s_int = reinterpret_cast<int32_t*>(dbg);
+  t.p_code = reinterpret_cast<int8_t*>(dbg + 64 * 64 * 4);
+  t.pv_int = reinterpret_cast<int32_t*>(dbg + 64 * 64 * 5);
+  t.m_after = reinterpret_cast<float*>(dbg + 64 * 64 * 5 + (size_t)64 * D * 4);
+  t.bh = b * p->shape.heads + h;
+  t.q_blk = q_blk;
+  t.kv_blk = kv_blk;
+  ra::launch_int4_tile_dump(a, t, D, stream);
+  st = after_launch("tile dump");
+  if (st != RA_OK) return st;
+  if (hipStreamSynchronize(stream) != hipSuccess) return fail(RA_ERR_HIP, "tile dump failed on device");
+  if (hipMemcpy(s_int, t.s_int, 64 * 64 * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(p_codes, t.p_code, 64 * 64, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(pv_int, t.pv_int, (size_t)64 * D * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(m_after, t.m_after, 64 * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(RA_ERR_HIP, "copy of tile dump failed");
+  return ok();
+}
+
+ra_status ra_debug_pmap(const float* x, uint8_t* u, int64_t n, hipStream_t stream) {
+  if (n < 0) return fail(RA_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 0 && (!x || !u)) return fail(RA_ERR_INVALID_ARG, "x and u must be non-null");
+  ra::launch_pmap_probe(x, u, n, stream);
+  ra_status st = after_launch("pmap probe");
+  return st == RA_OK ? ok() : st;
+}
+
+ra_status ra_debug_tables(ra_plan p, int32_t seg, float* cos_out, float* sin_out) {
+  if (!p || !cos_out || !sin_out) return fail(RA_ERR_INVALID_ARG, "null argument");
+  if (seg < 0 || seg > 2) return fail(RA_ERR_INVALID_ARG, "seg must be 0, 1 or 2");
+  std::memcpy(cos_out, p->cs[seg].data(), p->cs[seg].size() * sizeof(float));
+  std::memcpy(sin_out, p->sn[seg].data(), p->sn[seg].size() * sizeof(float));
+  return ok();
+}
+
+ra_status ra_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes && (!dst || !src)) return fail(RA_ERR_INVALID_ARG, "dst and src must be non-null");
+  if (misaligned(dst) || misaligned(src)) return fail(RA_ERR_ALIGNMENT, "dst and src must be 16-byte aligned");
+  ra::launch_copy(dst, src, bytes, stream);
+  ra_status st = after_launch("copy");
+  return st == RA_OK ? ok() : st;
+}
+
+}  // extern "C"

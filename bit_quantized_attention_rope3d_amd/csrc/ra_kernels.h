@@ -1,0 +1,66 @@
+// ra_kernels.h -- kernel argument blocks and host-side launchers (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "ra_common.h"
+
+namespace ra {
+
+struct QKPrologueArgs {
+  const void* q;      // [B, N, H, D] bf16 or f32
+  const void* k;
+  uint8_t* q_out;     // int4: [B*H, Npad, D/2] packed; bf16 path: [B*H, Npad, D] bf16
+  uint8_t* k_out;
+  float* s_q;         // [B*H, nblk] (int4 path only)
+  float* s_k;
+  RopeTabs tabs;
+  int B, N, H, Npad, nblk;
+};
+
+struct VAmaxArgs {
+  const void* v;
+  uint32_t* vamax;    // [B*H, D] float bits of the per-channel max |v|
+  int N, H, chunk;
+};
+
+struct VQuantArgs {
+  const void* v;
+  const uint32_t* vamax;
+  uint8_t* v_out;     // int4: [B*H, nkb, D, 32] packed; bf16: [B*H, nkb, D, 64] bf16
+  float* s_v;         // [B*H, D]
+  int N, H, nkb;
+};
+
+struct AttnArgs {
+  const uint8_t* qp;  // packed Q / K / V (int4) or bf16 tensors (bf16 path)
+  const uint8_t* kp;
+  const uint8_t* vp;
+  const float* s_q;
+  const float* s_k;
+  const float* s_v;
+  void* out;          // [B, N, H, D] f32 or bf16
+  int N, H, Npad, nblk, nkb, nqt;
+  float alpha_g;      // f32(log2(e) * softmax_scale * kPGrid)   (int4 path)
+  float alpha;        // f32(log2(e) * softmax_scale)            (bf16 path)
+};
+
+struct TileDumpArgs {
+  int32_t* s_int;     // [64, 64]
+  int8_t* p_code;     // [64, 64]
+  int32_t* pv_int;    // [64, D]
+  float* m_after;     // [64]
+  int bh, q_blk, kv_blk;
+};
+
+void launch_int4_prologue(const QKPrologueArgs& qa, const VAmaxArgs& va, const VQuantArgs& vq,
+                          int D, int rot, bool in_bf16, hipStream_t st);
+void launch_bf16_prologue(const QKPrologueArgs& qa, const VQuantArgs& vq, int D, bool in_bf16,
+                          hipStream_t st);
+void launch_int4_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
+void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipStream_t st);
+void launch_pmap_probe(const float* x, uint8_t* u, int64_t n, hipStream_t st);
+void launch_bf16_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
+void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+
+}  // namespace ra

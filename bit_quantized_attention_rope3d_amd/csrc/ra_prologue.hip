@@ -1,0 +1,383 @@
+// ra_prologue.hip -- prologue kernels: 3D RoPE + RoPE-aware rotation + INT4
+// quantization of Q/K, per-channel INT4 quantization of V, and the bf16
+// preparation used by the full-precision fallback.
+//
+// Method source: "RotateAttention: RoPE-Aware Rotation and Range Rectification
+// for INT4 Quantized Attention in Video Generation" (pith.science review):
+// Sec. 3 / Fig. 2 (frame/height/width RoPE segments), Sec. 4.1 / Fig. 3
+// (Interleaved rotation merged into RoPE, Half rotation with H2 blocks),
+// abstract (INT4 Q/K/V inside FlashAttention).  The 64-token Q/K scale block
+// follows the FlashAttention-tile-aligned blocks of the PAROAttention review.
+//
+// All kernels are HBM-bound streaming passes; every workgroup reads a 64-token
+// x D tile once (16-byte loads), does the arithmetic in fp32 registers/LDS and
+// writes packed output with 16-byte stores.
+#include "ra_common.h"
+#include "ra_kernels.h"
+
+namespace ra {
+
+template <bool BF16> struct InT;
+template <> struct InT<true> { typedef uint16_t T; };
+template <> struct InT<false> { typedef float T; };
+
+// Load one token row segment of `cnt` elements (cnt*sizeof(T) a multiple of
+// 16 bytes) starting at p into LDS row `dst` as fp32.
+template <bool BF16>
+__device__ __forceinline__ void load_row_part(const void* base, size_t elem_off, int cnt, float* dst) {
+  if (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
+    for (int i = 0; i < cnt / 8; ++i) {
+      uint4 w = p[i];
+      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[8 * i + 2 * e] = __uint_as_float(ws[e] << 16);
+        dst[8 * i + 2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
+    for (int i = 0; i < cnt / 4; ++i) {
+      float4 w = p[i];
+      dst[4 * i] = w.x; dst[4 * i + 1] = w.y; dst[4 * i + 2] = w.z; dst[4 * i + 3] = w.w;
+    }
+  }
+}
+
+// RoPE pair rotation of channel i (segment-relative) of the row at LDS `row`:
+// (a, b) -> (a c - b s, a s + b c), each product rounded before the sum.
+__device__ __forceinline__ float rope_at(const float* row, int o, int i, const float* cs, const float* sn) {
+  int j = i >> 1;
+  float a = row[o + 2 * j], b = row[o + 2 * j + 1];
+  float c = cs[j], s = sn[j];
+  if ((i & 1) == 0) {
+    float ac = a * c;
+    float bs = b * s;
+    return ac - bs;
+  }
+  float as = a * s;
+  float bc = b * c;
+  return as + bc;
+}
+
+// Rotated channel d: RoPE, then (ROT == 2) the Half rotation
+// u' = (u + w) r, w' = (u - w) r on (i, i + L/2), r = f32(1/sqrt 2).
+// ROT == 1 (Interleaved) is already merged into the tables as +pi/4.
+template <int ROT>
+__device__ __forceinline__ float rotated(const float* row, int d, const RopeTabs& t, const int* pos) {
+  int s = d < t.off[1] ? 0 : (d < t.off[2] ? 1 : 2);
+  int o = t.off[s], half = t.seg[s] >> 1;
+  int i = d - o;
+  const float* cs = t.cs[s] + (size_t)pos[s] * half;
+  const float* sn = t.sn[s] + (size_t)pos[s] * half;
+  if (ROT == 2) {
+    const float r = __uint_as_float(0x3F3504F3u);
+    if (i < half) {
+      float u = rope_at(row, o, i, cs, sn), w = rope_at(row, o, i + half, cs, sn);
+      float sum = u + w;
+      return sum * r;
+    }
+    float u = rope_at(row, o, i - half, cs, sn), w = rope_at(row, o, i, cs, sn);
+    float dif = u - w;
+    return dif * r;
+  }
+  return rope_at(row, o, i, cs, sn);
+}
+
+__device__ __forceinline__ int quant_code(float x, float inv) {
+  float q = __builtin_rintf(x * inv);
+  q = fminf(fmaxf(q, -7.0f), 7.0f);
+  return (int)q;
+}
+
+__device__ __forceinline__ float block_max_256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return m;
+}
+
+// ---------------------------------------------------------------------------
+// Q/K: one workgroup per (64-token block, b*h, tensor).  256 threads: thread
+// t owns row t/4 and channels (t%4)*D/4 .. +D/4.
+template <int ROT, bool BF16, int D>
+__global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
+  constexpr int PER = D / 4;
+  __shared__ float tile[64][D + 4];
+  __shared__ float red[4];
+  const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
+  const int b = bh / a.H, h = bh % a.H;
+  const void* x = which ? a.k : a.q;
+  uint8_t* out = which ? a.k_out : a.q_out;
+  float* sc = which ? a.s_k : a.s_q;
+
+  const int t = threadIdx.x, r = t >> 2, qq = t & 3;
+  const int n = blk * kBlock + r;
+  if (n < a.N) {
+    load_row_part<BF16>(x, (((size_t)b * a.N + n) * a.H + h) * D + qq * PER, PER, &tile[r][qq * PER]);
+  } else {
+    for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = 0.0f;
+  }
+  __syncthreads();
+
+  float y[PER];
+  float mx = 0.0f;
+  if (n < a.N) {
+    int pos[3];
+    pos[0] = n / (a.tabs.dims[1] * a.tabs.dims[2]);
+    pos[1] = (n / a.tabs.dims[2]) % a.tabs.dims[1];
+    pos[2] = n % a.tabs.dims[2];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      y[e] = rotated<ROT>(tile[r], qq * PER + e, a.tabs, pos);
+      mx = fmaxf(mx, fabsf(y[e]));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) y[e] = 0.0f;
+  }
+  const float amax = block_max_256(mx, red);
+  const float scale = amax / 7.0f;
+  const float inv = 7.0f / amax;
+
+  uint32_t packed[PER / 8];
+#pragma unroll
+  for (int g = 0; g < PER / 16; ++g) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        int i = half * 4 + bi;
+        int ch = amax > 0.0f ? quant_code(y[16 * g + i], inv) : 0;
+        int cl = amax > 0.0f ? quant_code(y[16 * g + i + 8], inv) : 0;
+        uint32_t byte = (((uint32_t)ch & 15u) << 4) | ((uint32_t)cl & 15u);
+        w |= byte << (8 * bi);
+      }
+      packed[2 * g + half] = w;
+    }
+  }
+  uint8_t* dst = out + ((size_t)bh * a.Npad + blk * kBlock + r) * (D / 2) + qq * (PER / 2);
+  if (PER / 2 == 16) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  } else {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+  }
+  if (t == 0) sc[(size_t)bh * a.nblk + blk] = amax > 0.0f ? scale : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// V per-channel amax over a chunk of tokens, merged with atomicMax on the
+// float bit pattern (order-preserving for non-negative floats).
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void k_v_amax(VAmaxArgs a) {
+  typedef typename InT<BF16>::T T;
+  constexpr int VEC = 16 / sizeof(T);      // elements per 16-byte load
+  constexpr int CG = D / VEC;              // threads per row
+  constexpr int PH = 256 / CG;             // rows per iteration
+  __shared__ float red[PH][D];
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int t = threadIdx.x, cg = t % CG, ph = t / CG;
+  const int n0 = blockIdx.x * a.chunk;
+  const int n1 = min(a.N, n0 + a.chunk);
+  float m[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) m[e] = 0.0f;
+  for (int n = n0 + ph; n < n1; n += PH) {
+    float v[VEC];
+    load_row_part<BF16>(a.v, (((size_t)b * a.N + n) * a.H + h) * D + cg * VEC, VEC, v);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) m[e] = fmaxf(m[e], fabsf(v[e]));
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) red[ph][cg * VEC + e] = m[e];
+  __syncthreads();
+  for (int d = t; d < D; d += 256) {
+    float mm = 0.0f;
+    for (int p = 0; p < PH; ++p) mm = fmaxf(mm, red[p][d]);
+    atomicMax(a.vamax + (size_t)bh * D + d, __float_as_uint(mm));
+  }
+}
+
+__global__ void k_zero_u32(uint32_t* p, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// V quantization + transpose into the PV operand layout: one workgroup per
+// (64-key block, b*h); thread t owns channel 4t/4.. and two 16-slot groups.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
+  constexpr int PER = D / 4;
+  __shared__ float tile[64][D + 1];
+  const int kb = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int t = threadIdx.x, r = t >> 2, qq = t & 3;
+  const int n = kb * kBlock + r;
+  float tmp[PER];
+  if (n < a.N) {
+    load_row_part<BF16>(a.v, (((size_t)b * a.N + n) * a.H + h) * D + qq * PER, PER, tmp);
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) tmp[e] = 0.0f;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = tmp[e];
+  __syncthreads();
+
+  constexpr int UNITS = D * 4 / 256;       // (channel, 16-slot group) units per thread
+#pragma unroll
+  for (int uu = 0; uu < UNITS; ++uu) {
+    const int unit = t * UNITS + uu;
+    const int d = unit >> 2, sg = unit & 3;
+    const float amax = __uint_as_float(a.vamax[(size_t)bh * D + d]);
+    const float inv = 7.0f / amax;
+    uint32_t w[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        int i = half * 4 + bi;
+        int kh = slot_key_i8(sg * 16 + i), kl = slot_key_i8(sg * 16 + i + 8);
+        int ch = amax > 0.0f ? quant_code(tile[kh][d], inv) : 0;
+        int cl = amax > 0.0f ? quant_code(tile[kl][d], inv) : 0;
+        acc |= ((((uint32_t)ch & 15u) << 4) | ((uint32_t)cl & 15u)) << (8 * bi);
+      }
+      w[half] = acc;
+    }
+    uint8_t* dst = a.v_out + (((size_t)bh * a.nkb + kb) * D + d) * 32 + sg * 8;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    if (kb == 0 && sg == 0) a.s_v[(size_t)bh * D + d] = amax > 0.0f ? amax / 7.0f : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 fallback preparation: RoPE in fp32 (no rotation, no quantization),
+// rounded to bf16, rows [b*h][Npad][D]; padded rows are zero.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void k_rope_bf16(QKPrologueArgs a) {
+  constexpr int PER = D / 4;
+  __shared__ float tile[64][D + 4];
+  const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
+  const int b = bh / a.H, h = bh % a.H;
+  const void* x = which ? a.k : a.q;
+  uint16_t* out = reinterpret_cast<uint16_t*>(which ? a.k_out : a.q_out);
+  const int t = threadIdx.x, r = t >> 2, qq = t & 3;
+  const int n = blk * kBlock + r;
+  if (n < a.N) {
+    load_row_part<BF16>(x, (((size_t)b * a.N + n) * a.H + h) * D + qq * PER, PER, &tile[r][qq * PER]);
+  } else {
+    for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = 0.0f;
+  }
+  __syncthreads();
+  uint32_t packed[PER / 2];
+  int pos[3] = {0, 0, 0};
+  if (n < a.N) {
+    pos[0] = n / (a.tabs.dims[1] * a.tabs.dims[2]);
+    pos[1] = (n / a.tabs.dims[2]) % a.tabs.dims[1];
+    pos[2] = n % a.tabs.dims[2];
+  }
+#pragma unroll
+  for (int e = 0; e < PER; e += 2) {
+    float y0 = n < a.N ? rotated<0>(tile[r], qq * PER + e, a.tabs, pos) : 0.0f;
+    float y1 = n < a.N ? rotated<0>(tile[r], qq * PER + e + 1, a.tabs, pos) : 0.0f;
+    packed[e / 2] = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + qq * PER);
+#pragma unroll
+  for (int i = 0; i < PER / 8; ++i)
+    dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+}
+
+// V for the bf16 path: per 64-key block, [d][64 slots] bf16 in the bf16 PV
+// operand slot order; padded keys are zero.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void k_v_bf16(VQuantArgs a) {
+  constexpr int PER = D / 4;
+  __shared__ float tile[64][D + 1];
+  const int kb = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int t = threadIdx.x, r = t >> 2, qq = t & 3;
+  const int n = kb * kBlock + r;
+  float tmp[PER];
+  if (n < a.N) {
+    load_row_part<BF16>(a.v, (((size_t)b * a.N + n) * a.H + h) * D + qq * PER, PER, tmp);
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) tmp[e] = 0.0f;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = tmp[e];
+  __syncthreads();
+  uint16_t* outp = reinterpret_cast<uint16_t*>(a.v_out);
+  constexpr int UNITS = D * 8 / 256;       // (channel, 8-slot group) units per thread
+#pragma unroll
+  for (int uu = 0; uu < UNITS; ++uu) {
+    const int unit = t * UNITS + uu;
+    const int d = unit >> 3, g = unit & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x0 = tile[slot_key_bf16(g * 8 + 2 * e)][d];
+      float x1 = tile[slot_key_bf16(g * 8 + 2 * e + 1)][d];
+      w[e] = (uint32_t)f32_to_bf16_bits(x0) | ((uint32_t)f32_to_bf16_bits(x1) << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(outp + (((size_t)bh * a.nkb + kb) * D + d) * 64 + g * 8);
+    *dst = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers.
+#define RA_DISPATCH_D(D_, ...)                      \
+  do {                                              \
+    if ((D_) == 128) { constexpr int D = 128; __VA_ARGS__; } \
+    else { constexpr int D = 64; __VA_ARGS__; }     \
+  } while (0)
+
+void launch_int4_prologue(const QKPrologueArgs& qa, const VAmaxArgs& va, const VQuantArgs& vq,
+                          int D, int rot, bool in_bf16, hipStream_t st) {
+  const int BH = qa.B * qa.H;
+  {
+    size_t n = (size_t)BH * D;
+    k_zero_u32<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(va.vamax, n);
+  }
+  dim3 gq(qa.nblk, BH, 2);
+  RA_DISPATCH_D(D, {
+    if (in_bf16) {
+      if (rot == 0) k_rope_quant_qk<0, true, D><<<gq, 256, 0, st>>>(qa);
+      else if (rot == 1) k_rope_quant_qk<1, true, D><<<gq, 256, 0, st>>>(qa);
+      else k_rope_quant_qk<2, true, D><<<gq, 256, 0, st>>>(qa);
+      k_v_amax<true, D><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
+      k_v_quant<true, D><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+    } else {
+      if (rot == 0) k_rope_quant_qk<0, false, D><<<gq, 256, 0, st>>>(qa);
+      else if (rot == 1) k_rope_quant_qk<1, false, D><<<gq, 256, 0, st>>>(qa);
+      else k_rope_quant_qk<2, false, D><<<gq, 256, 0, st>>>(qa);
+      k_v_amax<false, D><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
+      k_v_quant<false, D><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+    }
+  });
+}
+
+void launch_bf16_prologue(const QKPrologueArgs& qa, const VQuantArgs& vq, int D, bool in_bf16,
+                          hipStream_t st) {
+  const int BH = qa.B * qa.H;
+  dim3 gq(qa.nblk, BH, 2);
+  RA_DISPATCH_D(D, {
+    if (in_bf16) {
+      k_rope_bf16<true, D><<<gq, 256, 0, st>>>(qa);
+      k_v_bf16<true, D><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+    } else {
+      k_rope_bf16<false, D><<<gq, 256, 0, st>>>(qa);
+      k_v_bf16<false, D><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+    }
+  });
+}
+
+}  // namespace ra

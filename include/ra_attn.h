@@ -1,0 +1,183 @@
+/*
+ * ra_attn.h -- C ABI of libra_attn.so: RotateAttention INT4 FlashAttention
+ * forward for 3D-RoPE video diffusion transformers, on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (page: "RotateAttention: RoPE-Aware Rotation and Range
+ * Rectification for INT4 Quantized Attention in Video Generation",
+ * pith.science review of arXiv 2607.02584):
+ *   1. 3D RoPE over frame / height / width head-dim segments (Sec. 3, Fig. 2);
+ *   2. a RoPE-aware 2x2 orthogonal rotation of Q and K: Interleaved (merged
+ *      into the RoPE angles) or Half (pairs each dim with its counterpart in
+ *      the other half of its segment, H2 blocks) (Sec. 4.1, Fig. 3);
+ *   3. symmetric INT4 Q and K per (batch, head, 64-token block), symmetric
+ *      INT4 V per (batch, head, channel) (abstract);
+ *   4. online-softmax attention over 64-key steps, with the normalised P
+ *      mapped onto the whole signed INT4 range, code = round(15 p) - 8
+ *      (Sec. 4.2), and INT4 P x V;
+ *   5. a bf16 full-precision path for the accuracy-sensitive denoising steps
+ *      and DiT blocks (Sec. 5.1), selected per call.
+ *
+ * Conventions
+ *   * q, k, v, o are device pointers to [B, N, H, D] tensors, contiguous,
+ *     D fastest; N = F * H_grid * W tokens in (f, h, w) row-major order
+ *     (w fastest).  Input dtype bf16 or f32; output dtype f32 or bf16.
+ *   * All device pointers must be 16-byte aligned.
+ *   * The caller owns q, k, v, o and the workspace; the library never frees
+ *     them.  A plan owns only its RoPE tables (host copy, plus one small
+ *     device copy per GPU made on first use).
+ *   * Every entry point validates its arguments before enqueueing anything and
+ *     returns a status; on failure nothing is enqueued and
+ *     ra_last_error_message() (thread-local) says why.  Work is enqueued
+ *     asynchronously on `stream`; a device fault surfaces at the caller's
+ *     next synchronisation.
+ *   * A plan may be used from several threads / streams at once as long as
+ *     each call has its own workspace.
+ */
+#ifndef RA_ATTN_H
+#define RA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = 1,   /* null pointer, bad enum, bad index */
+  RA_ERR_SHAPE = 2,         /* non-positive or too large batch/heads/grid */
+  RA_ERR_SEGMENTS = 3,      /* segments not even, not positive, or not summing to D */
+  RA_ERR_DTYPE = 4,         /* unsupported input/output dtype */
+  RA_ERR_ALIGNMENT = 5,     /* a device pointer is not 16-byte aligned */
+  RA_ERR_WORKSPACE = 6,     /* workspace missing or smaller than required */
+  RA_ERR_UNSUPPORTED = 7,   /* valid request this build does not implement */
+  RA_ERR_OOM = 8,           /* device allocation of plan tables failed */
+  RA_ERR_HIP = 9            /* a HIP runtime call or kernel launch failed */
+} ra_status;
+
+typedef enum { RA_ROT_NONE = 0, RA_ROT_INTERLEAVED = 1, RA_ROT_HALF = 2 } ra_rot;
+typedef enum { RA_PREC_INT4 = 0, RA_PREC_BF16 = 1 } ra_prec;
+typedef enum { RA_DT_F32 = 0, RA_DT_BF16 = 1 } ra_dtype;
+
+/* Problem shape.  head_dim in {64, 128}; seg = (frame, height, width) even,
+ * positive, summing to head_dim. */
+typedef struct {
+  int32_t batch, heads, head_dim;
+  int32_t grid_f, grid_h, grid_w;
+  int32_t seg[3];
+} ra_shape;
+
+/* Options.  rope_theta: RoPE base (10000 in the pages' models; > 0).
+ * softmax_scale: 0 selects 1/sqrt(head_dim).  p_mode: 0 = range-optimized P
+ * (the only mode implemented; other values return RA_ERR_UNSUPPORTED). */
+typedef struct {
+  int32_t rot;        /* ra_rot */
+  int32_t prec;       /* ra_prec */
+  int32_t in_dtype;   /* ra_dtype of q, k, v */
+  int32_t out_dtype;  /* ra_dtype of o */
+  double rope_theta;
+  double softmax_scale;
+  int32_t p_mode;
+  int32_t reserved;
+} ra_opts;
+
+typedef struct ra_plan_s* ra_plan;
+
+/* Fill *opts with defaults: Half rotation, INT4, bf16 in, f32 out,
+ * theta 10000, scale 1/sqrt(D), range-optimized P. */
+ra_status ra_opts_default(ra_opts* opts);
+
+/* Validate shape/opts and build the RoPE cos/sin tables on the host (binary64
+ * angles, +pi/4 per pair for the merged Interleaved rotation, rounded to
+ * binary32).  No device work.  *out receives a plan to be destroyed with
+ * ra_plan_destroy. */
+ra_status ra_plan_create(const ra_shape* shape, const ra_opts* opts, ra_plan* out);
+
+/* Release the plan and its device table copies.  Null is accepted. */
+ra_status ra_plan_destroy(ra_plan plan);
+
+/* Workspace bytes one ra_attn_fwd call of this plan needs (packed INT4
+ * Q/K/V + scales, or the bf16 copies for the bf16 path). */
+ra_status ra_plan_workspace_size(ra_plan plan, size_t* bytes);
+
+/* Same figure without a plan. */
+ra_status ra_workspace_size(const ra_shape* shape, const ra_opts* opts, size_t* bytes);
+
+/* o = attention(q, k, v) for the plan's shape and options; enqueue only.
+ * Equivalent to ra_attn_prologue followed by ra_attn_main on the same
+ * workspace.  The first call on a device copies the plan's tables there
+ * (one small synchronous allocation + copy). */
+ra_status ra_attn_fwd(ra_plan plan, const void* q, const void* k, const void* v, void* o,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 1: RoPE + rotation + quantization (INT4) or RoPE + bf16 conversion
+ * (bf16 path) of q, k, v into the workspace. */
+ra_status ra_attn_prologue(ra_plan plan, const void* q, const void* k, const void* v,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 2: the attention kernel on a workspace filled by stage 1. */
+ra_status ra_attn_main(ra_plan plan, void* o, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* One-shot form: builds (and caches, under a mutex) a plan for these
+ * arguments with theta 10000 and scale 1/sqrt(D), then runs ra_attn_fwd. */
+ra_status ra_attn_fwd_simple(const void* q, const void* k, const void* v, void* o,
+                             int32_t batch, int32_t heads, int32_t head_dim,
+                             int32_t grid_f, int32_t grid_h, int32_t grid_w,
+                             int32_t seg_f, int32_t seg_h, int32_t seg_w,
+                             int32_t rot, int32_t prec, int32_t in_dtype, int32_t out_dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Mixed-precision schedule (Sec. 5.1): full precision on the first
+ * steps_head / last steps_tail sampling steps and on the first blocks_head /
+ * last blocks_tail DiT blocks (either condition), INT4 elsewhere. */
+typedef struct { int32_t steps_head, steps_tail, blocks_head, blocks_tail; } ra_schedule;
+ra_prec ra_schedule_pick(const ra_schedule* sched, int32_t step, int32_t n_steps,
+                         int32_t block, int32_t n_blocks);
+
+const char* ra_status_str(ra_status status);
+const char* ra_last_error_message(void);
+
+/* Steps per log2 unit of the grid on which the P exponent is rounded. */
+int32_t ra_pgrid(void);
+
+/* ---- parity / diagnostics exports (synchronous, test use) ---------------- */
+
+/* Run stage 1 of an INT4 plan into `workspace`, wait for it, and copy the
+ * quantized tensors to host buffers in plain layouts: codes [B, H, N, D] int8
+ * (q, k, v), s_q and s_k [B, H, ceil(N/64)], s_v [B, H, D]. */
+ra_status ra_debug_prologue(ra_plan plan, const void* q, const void* k, const void* v,
+                            void* workspace, size_t workspace_bytes,
+                            int8_t* q_codes, float* s_q, int8_t* k_codes, float* s_k,
+                            int8_t* v_codes, float* s_v, hipStream_t stream);
+
+/* On a workspace already filled by stage 1 of an INT4 plan, run the attention
+ * step code for the 64 queries of Q block q_blk of head (b, h) up to key step
+ * kv_blk and copy that step's exact integers to host buffers:
+ * s_int [64, 64] (query, key) scores, p_codes [64, 64] P codes in [-8, 7]
+ * (-8 for keys past N), pv_int [64, D] = sum_j code * vhat, m_after [64] the
+ * running max (grid units) after the step.  Rows past N are unspecified. */
+ra_status ra_debug_tile(ra_plan plan, void* workspace, size_t workspace_bytes,
+                        int32_t b, int32_t h, int32_t q_blk, int32_t kv_blk,
+                        int32_t* s_int, int8_t* p_codes, int32_t* pv_int, float* m_after,
+                        hipStream_t stream);
+
+/* Evaluate the kernels' P map on n grid exponents: x (device, f32) -> u = code
+ * + 8 (device, u8).  Enqueue only. */
+ra_status ra_debug_pmap(const float* x, uint8_t* u, int64_t n, hipStream_t stream);
+
+/* Host copy of the plan's binary32 RoPE table of segment `seg` (0 frame,
+ * 1 height, 2 width): cos and sin, each [positions, seg_len/2]. */
+ra_status ra_debug_tables(ra_plan plan, int32_t seg, float* cos_out, float* sin_out);
+
+/* Plain device-to-device copy kernel (bandwidth reference).  Enqueue only. */
+ra_status ra_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_ATTN_H */

@@ -1,0 +1,169 @@
+"""GPU parity of the HIP path against the CPU oracle (through the C ABI).
+
+Integer quantities (Q/K/V codes, scales, scores, P codes, PV sums, running
+max) must match bit for bit; the fp32 output must match the oracle's binary64
+float path within max-abs 2e-3 with cosine >= 0.999; the error against textbook
+fp64 attention is printed.  Shapes span several 64-token tiles with ragged
+tails; the full-size workloads are checked in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_attention_rope3d_amd import inputs
+from bit_quantized_attention_rope3d_amd.api import Plan, attn_fwd, pmap_device
+from oracle import ref_fp64
+
+from gpu_helpers import bf16_round, cosine, dev, plan_for, say
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+CASES = {
+    "tiny": inputs.get("tiny"),
+    "tiny_half": inputs.get("tiny").with_(name="tiny_half", rot="half"),
+    "tiny_none": inputs.get("tiny").with_(name="tiny_none", rot="none"),
+    "small": inputs.small(),                                             # 105 tokens, D128, bf16
+    "small_d64": inputs.small("small_d64", heads=2, head_dim=64, grid=(2, 7, 9), rot="interleaved",
+                              dtype="f32", seed=12),                     # 126 tokens
+    "medium": inputs.small("medium", heads=2, head_dim=128, grid=(3, 17, 23), rot="interleaved",
+                           seed=13),                                     # 1173 tokens, tail 21
+    "medium_out": inputs.Workload("medium_out", 1, 2, 128, (3, 16, 20), (44, 42, 42), rot="half",
+                                  seed=14, outliers_per_segment=(1, 1, 1)),   # 960 tokens
+    "batch2": inputs.small("batch2", heads=2, head_dim=128, grid=(2, 9, 11), rot="half", seed=15,
+                           batch=2),                                     # 198 tokens, B=2
+}
+
+
+def _prep(ora, w):
+    q, k, v, _ = inputs.generate(w)
+    pro = ora.prologue(q, k, v, w.grid, w.seg, w.theta, w.rot_id)
+    return q, k, v, pro
+
+
+def test_pmap_exhaustive(ora):
+    """Every grid exponent the kernels can produce (x <= 0) down to -2^23,
+    plus far-negative extremes, through the kernels' P-map device function."""
+    G = ora.pgrid()
+    x = np.arange(-(1 << 23), 1, dtype=np.int64).astype(np.float32)
+    extra = np.array([-np.inf, -3.0e38, -1.0e30, -2.0 ** 24, -2.0 ** 24 - 2, -1e9, -G, -G + 1, 0.0],
+                     np.float32)
+    x = np.concatenate([x, extra])
+    u_gpu = pmap_device(dev(x)).cpu().numpy()
+    u_ora = ora.pmap(x)
+    bad = np.nonzero(u_gpu != u_ora)[0]
+    say("pmap exhaustive: %d values, %d mismatches" % (x.size, bad.size))
+    assert bad.size == 0, (x[bad[:10]], u_gpu[bad[:10]], u_ora[bad[:10]])
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_prologue_bit_exact(ora, case):
+    w = CASES[case]
+    q, k, v, pro = _prep(ora, w)
+    p = plan_for(w)
+    got = p.debug_prologue(dev(q), dev(k), dev(v))
+    for key in ("q_codes", "k_codes", "v_codes"):
+        nbad = int((got[key] != pro[key]).sum())
+        assert nbad == 0, (case, key, nbad)
+    for key in ("s_q", "s_k", "s_v"):
+        assert np.array_equal(got[key].view(np.uint32), pro[key].view(np.uint32)), (case, key)
+    say("prologue %s: codes and scales bit-exact" % case)
+
+
+@pytest.mark.parametrize("case", ["tiny", "small", "small_d64", "medium", "medium_out", "batch2"])
+def test_tiles_bit_exact(ora, case):
+    w = CASES[case]
+    q, k, v, pro = _prep(ora, w)
+    p = plan_for(w)
+    ws = p.workspace()
+    p.prologue(dev(q), dev(k), dev(v), ws)
+    N = w.tokens
+    nb = (N + 63) // 64
+    rng = np.random.default_rng(0)
+    picks = {(0, 0), (nb - 1, nb - 1), (0, nb - 1), (nb - 1, 0), (nb // 2, nb // 2)}
+    picks |= {tuple(rng.integers(0, nb, 2).tolist()) for _ in range(3)}
+    for b in range(w.batch):
+        for h in sorted({0, w.heads - 1}):
+            for qb, kb in sorted(picks):
+                g = p.debug_tile(ws, b, h, qb, kb)
+                o = ora.attention_tile({kk: vv[b:b + 1] for kk, vv in pro.items()}, 0, h, qb, kb)
+                n = o["s_int"].shape[0]
+                nk = min(64, N - kb * 64)
+                assert np.array_equal(g["s_int"][:n, :nk], o["s_int"][:, :nk]), (case, b, h, qb, kb, "S")
+                assert np.array_equal(g["p_code"][:n], o["p_code"]), (case, b, h, qb, kb, "P")
+                assert np.array_equal(g["pv_int"][:n], o["pv_int"]), (case, b, h, qb, kb, "PV")
+                assert np.array_equal(g["m_after"][:n].view(np.uint32),
+                                      o["m_after"].view(np.uint32)), (case, b, h, qb, kb, "m")
+    say("tiles %s: %d tiles bit-exact" % (case, len(picks) * w.batch * len({0, w.heads - 1})))
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_output_matches_oracle(ora, case):
+    w = CASES[case]
+    q, k, v, pro = _prep(ora, w)
+    p = plan_for(w)
+    o = p.forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    want = ora.attention_full(pro)
+    err = np.abs(o - want).max()
+    cos = cosine(o, want)
+    ref = ref_fp64.reference_output(ora.as_f32(q), ora.as_f32(k), ora.as_f32(v), w.grid, w.seg, w.theta)
+    say("output %s: max|gpu-oracle| %.2e  cos %.7f | vs fp64 attention: max %.3e cos %.5f"
+        % (case, err, cos, np.abs(o - ref).max(), cosine(o, ref)))
+    assert err <= 2e-3 and cos >= 0.999
+
+
+def test_bf16_output_option(ora):
+    w = CASES["medium"]
+    q, k, v, pro = _prep(ora, w)
+    p = plan_for(w, out_dtype="bf16")
+    o = p.forward(dev(q), dev(k), dev(v)).float().cpu().numpy()
+    want = ora.attention_full(pro).astype(np.float32)
+    wb = bf16_round(want)
+    ulp = np.maximum(np.abs(wb), 1e-30) * 2.0 ** -7
+    assert np.all(np.abs(o - wb) <= ulp + 2e-3)
+
+
+def test_zero_queries_and_single_token(ora):
+    w = CASES["small"]
+    q, k, v, _ = inputs.generate(w)
+    q[:] = 0
+    pro = ora.prologue(q, k, v, w.grid, w.seg, w.theta, w.rot_id)
+    o = plan_for(w).forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    want = pro["s_v"][:, None, :, :] * pro["v_codes"].astype(np.float64).mean(axis=2)[:, None, :, :]
+    assert np.abs(o - want).max() <= 1e-5
+    w1 = inputs.Workload("one", 1, 3, 128, (1, 1, 1), (44, 42, 42), rot="half", seed=3)
+    q, k, v, _ = inputs.generate(w1)
+    pro = ora.prologue(q, k, v, w1.grid, w1.seg, w1.theta, w1.rot_id)
+    o = plan_for(w1).forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    want = pro["s_v"][:, None] * pro["v_codes"].astype(np.float64)[:, :, :1].transpose(0, 2, 1, 3)
+    assert np.abs(o - want).max() <= 1e-6
+
+
+def test_deterministic(ora):
+    w = CASES["medium"]
+    q, k, v, _ = inputs.generate(w)
+    p = plan_for(w)
+    a = p.forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    b = p.forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_simple_entry_point_matches_plan(ora):
+    w = CASES["small"]
+    q, k, v, _ = inputs.generate(w)
+    a = plan_for(w).forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    b = attn_fwd(dev(q), dev(k), dev(v), w.grid, w.seg, rot=w.rot).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("case", ["small", "small_d64", "medium", "medium_out"])
+def test_bf16_path_vs_fp64(ora, case):
+    w = CASES[case]
+    q, k, v, _ = inputs.generate(w)
+    o = plan_for(w, prec="bf16").forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    ref = ref_fp64.reference_output(ora.as_f32(q), ora.as_f32(k), ora.as_f32(v), w.grid, w.seg, w.theta)
+    err, cos = np.abs(o - ref).max(), cosine(o, ref)
+    say("bf16 path %s: max|gpu-fp64| %.3e cos %.7f" % (case, err, cos))
+    assert cos >= 0.9999 and err <= 2e-2
