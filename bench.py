@@ -46,7 +46,29 @@ def parse():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--main-only-steps", type=int, default=0,
                     help="extra launches of the attention kernel alone (profiling)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run the plain copy kernel on buffers of this size (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """Three launches of the library's plain copy kernel over `mib` MiB: the
+    reference that HBM byte counters are scaled against."""
+    import torch
+    from bit_quantized_attention_rope3d_amd.api import copy
+    n = mib * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        copy(dst, src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                      "gbs_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def kernel_hash():
@@ -134,6 +156,10 @@ def main():
         print("bench.py: this build runs on one GPU only (the attention shards by head with no "
               "collective; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
 
     import numpy as np
     import torch

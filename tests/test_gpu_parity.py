@@ -160,10 +160,19 @@ def test_simple_entry_point_matches_plan(ora):
 
 @pytest.mark.parametrize("case", ["small", "small_d64", "medium", "medium_out"])
 def test_bf16_path_vs_fp64(ora, case):
+    """The bf16 fallback against fp64 attention on the same bf16-rounded RoPE'd
+    Q/K (the fallback's only input rounding); the remaining error is P rounded
+    to bf16 and fp32 accumulation.  The error against exact fp64 attention of
+    the unrounded inputs is printed as well."""
     w = CASES[case]
     q, k, v, _ = inputs.generate(w)
     o = plan_for(w, prec="bf16").forward(dev(q), dev(k), dev(v)).cpu().numpy()
-    ref = ref_fp64.reference_output(ora.as_f32(q), ora.as_f32(k), ora.as_f32(v), w.grid, w.seg, w.theta)
+    qf, kf, vf = ora.as_f32(q), ora.as_f32(k), ora.as_f32(v)
+    qr = bf16_round(ref_fp64.rope3d(qf, w.grid, w.seg, w.theta).astype(np.float32))
+    kr = bf16_round(ref_fp64.rope3d(kf, w.grid, w.seg, w.theta).astype(np.float32))
+    ref = ref_fp64.attention(qr, kr, bf16_round(vf))
+    exact = ref_fp64.reference_output(qf, kf, vf, w.grid, w.seg, w.theta)
     err, cos = np.abs(o - ref).max(), cosine(o, ref)
-    say("bf16 path %s: max|gpu-fp64| %.3e cos %.7f" % (case, err, cos))
+    say("bf16 path %s: vs fp64 on bf16 inputs max %.3e cos %.7f | vs exact fp64 max %.3e cos %.6f"
+        % (case, err, cos, np.abs(o - exact).max(), cosine(o, exact)))
     assert cos >= 0.9999 and err <= 2e-2
