@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-KERNEL_SOURCE = os.path.join(ROOT, "bit_quantized_attention_rope3d_amd", "csrc", "ra_int4_attn.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_attention_rope3d_amd", "csrc", f)
+                  for f in ("ra_int4_attn.hip", "ra_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_int4_flash_fwd_wan720.json")
 
 
@@ -72,8 +73,13 @@ def copy_calibration(mib):
 
 
 def kernel_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernel's sources: a stored traffic figure is only
+    used while the kernel it was measured on is unchanged."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for_current_kernel():

@@ -8,6 +8,7 @@
 namespace ra {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -31,9 +32,11 @@ constexpr float kLog2Of15 = (float)3.9068905956085187;
 // kernels (readers):
 //   * Q/K rows: D/2 bytes per token; 16-channel group g occupies bytes
 //     8g..8g+7, byte i of a group holds channel 16g+i in its high nibble and
-//     channel 16g+i+8 in its low nibble (two's-complement nibbles).
+//     channel 16g+i+8 in its low nibble.  Nibbles are sign-magnitude
+//     (bit 3 = sign, bits 0-2 = |code|; codes lie in [-7, 7]).
 //   * V tile of one 64-key block: for each channel d, 32 bytes holding the 64
-//     key slots in MFMA operand order, grouped by 16 slots like Q/K rows.
+//     key slots in MFMA operand order, grouped by 16 slots like Q/K rows,
+//     nibbles in two's complement.
 //   Slot s = 32*ks + 16*hf + j carries key 32*ks + 8*(j/4) + 4*hf + (j%4):
 //   the key that the 32x32 MFMA accumulator of S^T = K Q^T leaves in
 //   register j of the lane half hf, so P feeds the PV MFMA with no shuffle.
@@ -48,11 +51,22 @@ __host__ __device__ constexpr int slot_key_bf16(int slot) {
          4 * ((slot >> 3) & 1) + (slot & 3);
 }
 
-// Widen 8 packed nibble codes (one dword) to 16*code int8 values:
-// high nibbles -> bytes of `hi`, low nibbles -> bytes of `lo`.
+// Widen 8 packed two's-complement nibble codes (one dword) to 16*code int8
+// values: high nibbles -> bytes of `hi`, low nibbles -> bytes of `lo`.
 __device__ __forceinline__ void unpack_x16(uint32_t w, uint32_t& hi, uint32_t& lo) {
   hi = w & 0xF0F0F0F0u;
   lo = (w << 4) & 0xF0F0F0F0u;
+}
+
+// Widen 8 packed sign-magnitude nibble codes to OCP fp8 e4m3 bytes (exact for
+// |code| <= 7): the magnitude indexes a byte table with v_perm, the sign bit
+// moves to bit 7.  e4m3 of 0..7 = 00 38 40 44 48 4A 4C 4E.
+__device__ __forceinline__ void unpack_e4m3(uint32_t w, uint32_t& hi, uint32_t& lo) {
+  const uint32_t t_lo = 0x44403800u, t_hi = 0x4E4C4A48u;
+  const uint32_t mh = (w >> 4) & 0x07070707u;
+  const uint32_t ml = w & 0x07070707u;
+  hi = (w & 0x80808080u) | __builtin_amdgcn_perm(t_hi, t_lo, mh);
+  lo = ((w << 4) & 0x80808080u) | __builtin_amdgcn_perm(t_hi, t_lo, ml);
 }
 
 // Range-optimized P code, as u = code + 8 in [0, 15], of the grid exponent

@@ -468,9 +468,13 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
       hipMemcpy(s_k, w + L.off_sk, BH * L.nblk * 4, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(s_v, w + L.off_sv, BH * D * 4, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(RA_ERR_HIP, "copy of prologue outputs failed");
-  auto nib = [](uint8_t byte, bool high) -> int8_t {
+  auto nib = [](uint8_t byte, bool high) -> int8_t {     // two's complement (V)
     int x = high ? (byte >> 4) : (byte & 15);
     return (int8_t)(x >= 8 ? x - 16 : x);
+  };
+  auto nib_sm = [](uint8_t byte, bool high) -> int8_t {  // sign-magnitude (Q, K)
+    int x = high ? (byte >> 4) : (byte & 15);
+    return (int8_t)((x & 8) ? -(x & 7) : x);
   };
   // Q/K rows: group g of 16 channels, byte i -> channel 16g+i (high), 16g+i+8 (low).
   for (size_t bh = 0; bh < BH; ++bh)
@@ -481,10 +485,10 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
       int8_t* ok_ = k_codes + (bh * N + n) * D;
       for (int g = 0; g < D / 16; ++g)
         for (int i = 0; i < 8; ++i) {
-          oq[16 * g + i] = nib(rq[8 * g + i], true);
-          oq[16 * g + i + 8] = nib(rq[8 * g + i], false);
-          ok_[16 * g + i] = nib(rk[8 * g + i], true);
-          ok_[16 * g + i + 8] = nib(rk[8 * g + i], false);
+          oq[16 * g + i] = nib_sm(rq[8 * g + i], true);
+          oq[16 * g + i + 8] = nib_sm(rq[8 * g + i], false);
+          ok_[16 * g + i] = nib_sm(rk[8 * g + i], true);
+          ok_[16 * g + i + 8] = nib_sm(rk[8 * g + i], false);
         }
     }
   // V: per 64-key block and channel, 64 slots in operand order.

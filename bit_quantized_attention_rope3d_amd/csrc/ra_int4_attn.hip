@@ -13,8 +13,11 @@
 //     are fetched with one 16-byte load per thread, widened once per
 //     workgroup to int8 (x16, a shift and two masks per 8 codes) into LDS
 //     (XOR-swizzled rows, no padding), double-buffered, one barrier per step.
-//   * S^T = K Q^T on v_mfma_i32_32x32x32_i8 (exact INT32): each lane holds one
-//     query column, so row max / row sum are in-lane (+1 cross-half swap).
+//   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 with the INT4 codes widened to
+//     fp8 e4m3 (exact for |code| <= 7; every partial sum is an integer below
+//     2^24, so the fp32 accumulator holds the exact integer score and no
+//     int->float conversion is needed).  Each lane holds one query column, so
+//     row max / row sum are in-lane (+1 cross-half swap).
 //   * P codes come straight out of the accumulator registers as bytes
 //     (exponent FMA, round, exp2, cvt_pk_u8) in the order the PV MFMA wants
 //     them as its B operand; V is stored pre-permuted to match.
@@ -30,23 +33,26 @@ namespace ra {
 
 template <int D>
 struct Cfg {
-  static constexpr int KC = D / 32;        // 32-channel chunks of the Q.K contraction
+  static constexpr int QC = D / 64;        // 64-channel chunks of the Q.K contraction
   static constexpr int DT = D / 32;        // 32-channel tiles of O
-  static constexpr int KT = 64 * D;        // int8 K tile: 64 rows of D bytes
+  static constexpr int KT = 64 * D;        // fp8 K tile: 64 rows of D bytes
   static constexpr int VT = D * 64;        // int8 V tile: D rows of 64 slots
-  static constexpr int STAGE = KT + VT;
   static constexpr int KPARTS = D / 32;    // 16-byte packed parts per key row
   static constexpr int KP = 64 * KPARTS;   // packed K parts per tile
   static constexpr int TOT = KP + 2 * D;   // + packed V parts (2 per channel)
   static constexpr int ACCF = DT * 4 * 64 * 16;   // LDS bytes of one wave's fp32 accumulator
 };
 
-// LDS rows are XOR-swizzled in 16-byte chunks so that the 8 lanes served per
-// LDS cycle by a ds_read_b128 of consecutive rows hit distinct bank groups.
+// LDS rows are XOR-swizzled in 16-byte chunks.  The gfx950 LDS serves a
+// ds_read_b128 / ds_write_b128 in groups of 16 lanes over 64 banks (256 B);
+// the operand reads of one group touch 16 consecutive rows at one logical
+// chunk, so the swizzle must give those 16 rows 16 distinct 16-byte slots
+// of the 256-byte bank window: row parity (128-byte rows) or row mod 4
+// (64-byte rows) picks the half / quarter, the XOR picks the slot within it.
 template <int ROWBYTES>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  if (ROWBYTES == 128) return row * 128 + ((chunk ^ (row & 7)) << 4);
-  return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
+  if (ROWBYTES == 128) return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 template <int D>
@@ -58,26 +64,31 @@ struct State {
   float* accf;              // this wave's fp32 accumulator in LDS: [DT*4][64 lanes][4]
 };
 
+// Cooperative fetch of packed tiles into registers and widening store into
+// LDS.  The K part and the V part may belong to different key steps (the
+// pipelined main loop keeps K one step ahead of V); a negative index skips it.
 template <int D, int NT>
 struct TileLoad {
   static constexpr int NP = (Cfg<D>::TOT + NT - 1) / NT;
   static constexpr bool EXACT = Cfg<D>::TOT % NT == 0;
   v4u r[NP];
 
-  __device__ __forceinline__ void fetch(const AttnArgs& a, int bh, int kb) {
+  __device__ __forceinline__ void fetch(const AttnArgs& a, int bh, int kt, int vt) {
     using C = Cfg<D>;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int p = threadIdx.x + i * NT;
       const int pv = p - C::KP;
-      const uint8_t* src = p < C::KP
-          ? a.kp + ((size_t)bh * a.Npad + (size_t)kb * kBlock + p / C::KPARTS) * (D / 2) + (p % C::KPARTS) * 16
-          : a.vp + (((size_t)bh * a.nkb + kb) * D + (pv >> 1)) * 32 + (pv & 1) * 16;
-      if (EXACT || p < C::TOT) r[i] = *reinterpret_cast<const v4u*>(src);
+      const bool isk = p < C::KP;
+      const int t = isk ? kt : vt;
+      const uint8_t* src = isk
+          ? a.kp + ((size_t)bh * a.Npad + (size_t)kt * kBlock + p / C::KPARTS) * (D / 2) + (p % C::KPARTS) * 16
+          : a.vp + (((size_t)bh * a.nkb + vt) * D + (pv >> 1)) * 32 + (pv & 1) * 16;
+      if ((EXACT || p < C::TOT) && t >= 0) r[i] = *reinterpret_cast<const v4u*>(src);
     }
   }
 
-  __device__ __forceinline__ void store(uint8_t* stage) const {
+  __device__ __forceinline__ void store(uint8_t* kst, uint8_t* vst, bool do_k, bool do_v) const {
     using C = Cfg<D>;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -85,35 +96,46 @@ struct TileLoad {
       if (!EXACT && p >= C::TOT) continue;
       const int pv = p - C::KP;
       const bool isk = p < C::KP;
+      if (isk ? !do_k : !do_v) continue;
       const int row = isk ? p / C::KPARTS : (pv >> 1);
       const int c0 = 2 * (isk ? p % C::KPARTS : (pv & 1));
       uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-      unpack_x16(r[i][0], h0, l0);
-      unpack_x16(r[i][1], h1, l1);
-      unpack_x16(r[i][2], h2, l2);
-      unpack_x16(r[i][3], h3, l3);
-      const int o0 = isk ? swz<D>(row, c0) : C::KT + swz<64>(row, c0);
-      const int o1 = isk ? swz<D>(row, c0 + 1) : C::KT + swz<64>(row, c0 + 1);
-      *reinterpret_cast<v4u*>(stage + o0) = v4u{h0, h1, l0, l1};
-      *reinterpret_cast<v4u*>(stage + o1) = v4u{h2, h3, l2, l3};
+      if (isk) {            // K codes -> fp8 e4m3 (QK runs on the fp8 MFMA)
+        unpack_e4m3(r[i][0], h0, l0);
+        unpack_e4m3(r[i][1], h1, l1);
+        unpack_e4m3(r[i][2], h2, l2);
+        unpack_e4m3(r[i][3], h3, l3);
+      } else {              // V codes -> 16 * code int8 (PV runs on the i8 MFMA)
+        unpack_x16(r[i][0], h0, l0);
+        unpack_x16(r[i][1], h1, l1);
+        unpack_x16(r[i][2], h2, l2);
+        unpack_x16(r[i][3], h3, l3);
+      }
+      uint8_t* base = isk ? kst : vst;
+      const int o0 = isk ? swz<D>(row, c0) : swz<64>(row, c0);
+      const int o1 = isk ? swz<D>(row, c0 + 1) : swz<64>(row, c0 + 1);
+      *reinterpret_cast<v4u*>(base + o0) = v4u{h0, h1, l0, l1};
+      *reinterpret_cast<v4u*>(base + o1) = v4u{h2, h3, l2, l3};
     }
   }
 };
 
-// Q operands (B operand of S^T = K Q^T): query `q`, channels 32kc + 16hf + 0..15.
+// Q operands (B operand of S^T = K Q^T on the fp8 MFMA): query `q`,
+// channels 64qc + 32hf + 0..31 as e4m3 bytes.
 template <int D>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int bh, int q, int hf,
-                                       v4i (&qop)[Cfg<D>::KC]) {
+                                       v8i (&qop)[Cfg<D>::QC]) {
 #pragma unroll
-  for (int kc = 0; kc < Cfg<D>::KC; ++kc) {
-    uint2 w = make_uint2(0u, 0u);
+  for (int qc = 0; qc < Cfg<D>::QC; ++qc) {
+    v4u w = v4u{0u, 0u, 0u, 0u};
     if (q < a.Npad)
-      w = *reinterpret_cast<const uint2*>(a.qp + ((size_t)bh * a.Npad + q) * (D / 2) +
-                                          (kc * 2 + hf) * 8);
-    uint32_t h0, l0, h1, l1;
-    unpack_x16(w.x, h0, l0);
-    unpack_x16(w.y, h1, l1);
-    qop[kc] = v4i{(int)h0, (int)h1, (int)l0, (int)l1};
+      w = *reinterpret_cast<const v4u*>(a.qp + ((size_t)bh * a.Npad + q) * (D / 2) + (qc * 4 + hf * 2) * 8);
+    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+    unpack_e4m3(w[0], h0, l0);
+    unpack_e4m3(w[1], h1, l1);
+    unpack_e4m3(w[2], h2, l2);
+    unpack_e4m3(w[3], h3, l3);
+    qop[qc] = v8i{(int)h0, (int)h1, (int)l0, (int)l1, (int)h2, (int)h3, (int)l2, (int)l3};
   }
 }
 
@@ -122,104 +144,145 @@ __device__ __forceinline__ int acc_key(int mt, int r, int hf) {
   return mt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
 }
 
-// One 64-key step for the 32 queries of this wave.
-template <int D, bool DUMP>
-__device__ __forceinline__ void tile_step(const uint8_t* stage, const v4i (&qop)[Cfg<D>::KC],
-                                          float cq, float alpha_g, float sk, int nvalid,
-                                          State<D>& st, const TileDumpArgs* dump, int wave) {
-  using C = Cfg<D>;
-  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
+// ---- building blocks of one 64-key step for the 32 queries of a wave ------
 
-  // S^T (x256) for keys of the step, queries of the wave.
-  v16i s[2];
+// S^T of the step (exact integers in fp32): kst is the step's fp8 K tile.
+template <int D>
+__device__ __forceinline__ void qk_step(const uint8_t* kst, const v8i (&qop)[Cfg<D>::QC], v16f (&s)[2]) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    s[mt] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-      const v4i ka = *reinterpret_cast<const v4i*>(stage + swz<D>(mt * 32 + ln, kc * 2 + hf));
-      s[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qop[kc], s[mt], 0, 0, 0);
+    for (int r = 0; r < 16; ++r) s[mt][r] = 0.0f;
+#pragma unroll
+    for (int qc = 0; qc < Cfg<D>::QC; ++qc) {
+      const int row = mt * 32 + ln, c0 = qc * 4 + hf * 2;
+      const v4i k0 = *reinterpret_cast<const v4i*>(kst + swz<D>(row, c0));
+      const v4i k1 = *reinterpret_cast<const v4i*>(kst + swz<D>(row, c0 + 1));
+      const v8i ka = v8i{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+      s[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qop[qc], s[mt], 0, 0, 0, 0, 0, 0);
     }
   }
-  if (nvalid < kBlock) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (acc_key(mt, r, hf) >= nvalid) s[mt][r] = INT32_MIN;
-  }
+}
 
-  // Running max on the integer scores; one rounding-up conversion per row.
-  int mx = s[0][0];
+// Keys at or past `nvalid` (ragged last step) are excluded from the max.
+__device__ __forceinline__ void mask_scores(v16f (&s)[2], int nvalid) {
+  const int hf = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = max(mx, s[mt][r]);
-  mx = xhalf_max_i(mx);
-  const float sqk = cq * sk;
-  const float c = sqk * alpha_g;
-  const float cp = c * 0.00390625f;           // scores carry a factor 256
-  const float m_step = mul_round_up((float)mx, cp);
-  const float m_new = fmaxf(st.m, m_step);
-  if (__ballot(m_new > st.m) != 0) {
-    const float beta = exp2f((st.m - m_new) * kInvPGrid);
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        v4f* pa = reinterpret_cast<v4f*>(st.accf) + (dt * 4 + g) * 64 + lane;
-        v4f acc = *pa;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] = (acc[e] + (float)st.acc_i[dt][4 * g + e]) * beta;
-          st.acc_i[dt][4 * g + e] = 0;
-        }
-        *pa = acc;
-      }
-    st.L = (st.L + (float)st.U) * beta;
-    st.U = 0u;
-  }
-  st.m = m_new;
+    for (int r = 0; r < 16; ++r)
+      if (acc_key(mt, r, hf) >= nvalid) s[mt][r] = -INFINITY;
+}
 
-  // P codes (u = code + 8) as bytes: dword j/4 of M-tile mt holds registers
-  // 4(j/4)..4(j/4)+3, i.e. the B operand of the PV MFMA for K-step mt.
-  uint32_t p[2][4];
+// Running-max candidate of the step for this lane's query (grid units):
+// the smallest float >= max_j S_j * c.
+__device__ __forceinline__ float step_max(const v16f (&s)[2], float c) {
+  float mx = s[0][0];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t acc = 0u;
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+  mx = xhalf_max_f(mx);
+  return mul_round_up(mx, c);
+}
+
+// P codes of M-tile mt (u = code + 8) as the 16-byte B operand of the PV MFMA.
+__device__ __forceinline__ void pmap_mtile(const v16f& s, float c, float m, uint32_t (&p)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float dlt = __builtin_fmaf(s[4 * i + e], c, -m);
+      const float x = __builtin_rintf(dlt);
+      acc = pmap_insert(x, (uint32_t)e, acc);
+    }
+    p[i] = acc;
+  }
+}
+
+__device__ __forceinline__ void mask_codes(uint32_t (&p)[2][4], int nvalid) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (acc_key(mt, r, hf) >= nvalid) p[mt][r >> 2] &= ~(0xFFu << (8 * (r & 3)));
+}
+
+__device__ __forceinline__ uint32_t code_sum(const uint32_t (&p)[4], uint32_t U) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) U = __builtin_amdgcn_sad_u8(p[i], 0u, U);
+  return U;
+}
+
+// O^T += V^T P^T for K-step ks (keys 32ks..32ks+31) of the step.
+template <int D>
+__device__ __forceinline__ void pv_kstep(const uint8_t* vst, const uint32_t (&p)[4], int ks,
+                                         v16i (&acc)[Cfg<D>::DT]) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
+  const v4i pb = v4i{(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
+#pragma unroll
+  for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
+    const v4i va = *reinterpret_cast<const v4i*>(vst + swz<64>(dt * 32 + ln, ks * 2 + hf));
+    acc[dt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, pb, acc[dt], 0, 0, 0);
+  }
+}
+
+// The running max rises from st.m to m_new: fold the integer accumulator into
+// the fp32 one with the rescale, A = (A + I) * beta, L = (L + U) * beta.
+template <int D>
+__device__ __forceinline__ void rescale(State<D>& st, float m_new) {
+  const int lane = threadIdx.x & 63;
+  const float beta = exp2f((st.m - m_new) * kInvPGrid);
+#pragma unroll
+  for (int dt = 0; dt < Cfg<D>::DT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      v4f* pa = reinterpret_cast<v4f*>(st.accf) + (dt * 4 + g) * 64 + lane;
+      v4f acc = *pa;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float f = (float)s[mt][4 * i + e];
-        const float dlt = __builtin_fmaf(f, cp, -m_new);
-        const float x = __builtin_rintf(dlt);
-        acc = pmap_insert(x, (uint32_t)e, acc);
+        acc[e] = (acc[e] + (float)st.acc_i[dt][4 * g + e]) * beta;
+        st.acc_i[dt][4 * g + e] = 0;
       }
-      p[mt][i] = acc;
+      *pa = acc;
     }
-  if (nvalid < kBlock) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (acc_key(mt, r, hf) >= nvalid) p[mt][r >> 2] &= ~(0xFFu << (8 * (r & 3)));
-  }
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.U = __builtin_amdgcn_sad_u8(p[mt][i], 0u, st.U);
+  st.L = (st.L + (float)st.U) * beta;
+  st.U = 0u;
+}
 
-  // O^T += V^T P^T in INT32.
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const v4i pb = v4i{(int)p[ks][0], (int)p[ks][1], (int)p[ks][2], (int)p[ks][3]};
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const v4i va = *reinterpret_cast<const v4i*>(stage + C::KT + swz<64>(dt * 32 + ln, ks * 2 + hf));
-      st.acc_i[dt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, pb, st.acc_i[dt], 0, 0, 0);
-    }
-  }
+// c = f32(f32(s_q s_k) alpha_G): grid units per unit of integer score.
+__device__ __forceinline__ float score_scale(float cq, float sk, float alpha_g) {
+  const float sqk = cq * sk;
+  return sqk * alpha_g;
+}
+
+// One whole 64-key step in program order (used by the parity dump kernel;
+// the main kernel runs the same blocks software-pipelined).
+template <int D, bool DUMP>
+__device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst,
+                                          const v8i (&qop)[Cfg<D>::QC], float cq, float alpha_g,
+                                          float sk, int nvalid, State<D>& st,
+                                          const TileDumpArgs* dump, int wave) {
+  using C = Cfg<D>;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
+  v16f s[2];
+  qk_step<D>(kst, qop, s);
+  if (nvalid < kBlock) mask_scores(s, nvalid);
+  const float cp = score_scale(cq, sk, alpha_g);
+  const float m_new = fmaxf(st.m, step_max(s, cp));
+  if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
+  st.m = m_new;
+  uint32_t p[2][4];
+  pmap_mtile(s[0], cp, m_new, p[0]);
+  pmap_mtile(s[1], cp, m_new, p[1]);
+  if (nvalid < kBlock) mask_codes(p, nvalid);
+  st.U = code_sum(p[0], st.U);
+  st.U = code_sum(p[1], st.U);
+  pv_kstep<D>(vst, p[0], 0, st.acc_i);
+  pv_kstep<D>(vst, p[1], 1, st.acc_i);
 
   if (DUMP) {
     // Exact per-step integers: S, P codes, PV = sum (u - 8) vhat, running max.
@@ -234,7 +297,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, const v4i (&qop)
         const int key = acc_key(mt, r, hf);
         if (r % 4 == 0) ones[mt][r >> 2] = 0u;
         if (key < nvalid) ones[mt][r >> 2] |= 1u << (8 * (r & 3));
-        const int sv = key < nvalid ? (s[mt][r] >> 8) : 0;
+        const int sv = key < nvalid ? (int)s[mt][r] : 0;
         const int code = (int)((p[mt][r >> 2] >> (8 * (r & 3))) & 0xFFu) - 8;
         dump->s_int[qrow * 64 + key] = sv;
         dump->p_code[qrow * 64 + key] = (int8_t)code;
@@ -243,14 +306,8 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, const v4i (&qop)
     for (int dt = 0; dt < C::DT; ++dt) { pv[dt] = z; cs[dt] = z; }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const v4i pb = v4i{(int)p[ks][0], (int)p[ks][1], (int)p[ks][2], (int)p[ks][3]};
-      const v4i ob = v4i{(int)ones[ks][0], (int)ones[ks][1], (int)ones[ks][2], (int)ones[ks][3]};
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const v4i va = *reinterpret_cast<const v4i*>(stage + C::KT + swz<64>(dt * 32 + ln, ks * 2 + hf));
-        pv[dt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, pb, pv[dt], 0, 0, 0);
-        cs[dt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, ob, cs[dt], 0, 0, 0);
-      }
+      pv_kstep<D>(vst, p[ks], ks, pv);
+      pv_kstep<D>(vst, ones[ks], ks, cs);
     }
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -282,7 +339,9 @@ __device__ __forceinline__ void state_init(State<D>& st, float* accf) {
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE + 8 * C::ACCF];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::KT + 2 * C::VT + 8 * C::ACCF];
+  uint8_t* const kbuf = smem;                     // 2 K stages
+  uint8_t* const vbuf = smem + 2 * C::KT;         // 2 V stages
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of (head, query-tile) ids.
@@ -294,27 +353,71 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const int q0 = qt * 256 + wave * 32;
   const int qblk = q0 >> 6;
+  const int nkb = a.nkb;
 
-  v4i qop[C::KC];
+  v8i qop[C::QC];
   load_q<D>(a, bh, q0 + ln, hf, qop);
   const float cq = qblk < a.nblk ? a.s_q[(size_t)bh * a.nblk + qblk] : 0.0f;
+  const float* sk = a.s_k + (size_t)bh * a.nblk;
 
   State<D> st;
-  state_init<D>(st, reinterpret_cast<float*>(smem + 2 * C::STAGE + wave * C::ACCF));
+  state_init<D>(st, reinterpret_cast<float*>(smem + 2 * C::KT + 2 * C::VT + wave * C::ACCF));
 
+  // Pipeline: during step t the wave computes S of step t+1 (K one stage
+  // ahead) while it turns S of step t into P codes, then P x V of step t;
+  // one barrier per step.  K of step t+2 and V of step t+1 are fetched
+  // during step t and widened into the stages freed by step t-1.
   TileLoad<D, 512> ld;
-  ld.fetch(a, bh, 0);
-  ld.store(smem);
+  ld.fetch(a, bh, 0, -1);
+  ld.store(kbuf, vbuf, true, false);
   __syncthreads();
-  for (int kb = 0; kb < a.nkb; ++kb) {
-    const bool more = kb + 1 < a.nkb;
-    if (more) ld.fetch(a, bh, kb + 1);
-    const int nvalid = min(kBlock, a.N - kb * kBlock);
-    const float sk = a.s_k[(size_t)bh * a.nblk + kb];
-    tile_step<D, false>(smem + (kb & 1) * C::STAGE, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave);
-    if (more) ld.store(smem + ((kb + 1) & 1) * C::STAGE);
+  ld.fetch(a, bh, nkb > 1 ? 1 : -1, 0);
+  v16f s_cur[2];
+  qk_step<D>(kbuf, qop, s_cur);
+  const int nv0 = min(kBlock, a.N);
+  if (nv0 < kBlock) mask_scores(s_cur, nv0);
+  float cp_cur = score_scale(cq, sk[0], a.alpha_g);
+  st.m = step_max(s_cur, cp_cur);
+  ld.store(kbuf + C::KT, vbuf, nkb > 1, true);
+  __syncthreads();
+
+  // One pipelined step; the two score register sets swap roles every step
+  // (the loop is unrolled by two so that no copy is needed).
+  auto step = [&](v16f (&sc)[2], v16f (&sn)[2], int t) {
+    ld.fetch(a, bh, t + 2 < nkb ? t + 2 : -1, t + 1 < nkb ? t + 1 : -1);
+    const uint8_t* kst = kbuf + ((t + 1) & 1) * C::KT;
+    const uint8_t* vst = vbuf + (t & 1) * C::VT;
+
+    qk_step<D>(kst, qop, sn);                     // S of step t+1 (unused after the last step)
+    uint32_t p[2][4];
+    pmap_mtile(sc[0], cp_cur, st.m, p[0]);
+    pmap_mtile(sc[1], cp_cur, st.m, p[1]);
+    const int nvalid = min(kBlock, a.N - t * kBlock);
+    if (nvalid < kBlock) mask_codes(p, nvalid);
+    st.U = code_sum(p[0], st.U);
+    st.U = code_sum(p[1], st.U);
+    pv_kstep<D>(vst, p[0], 0, st.acc_i);
+    pv_kstep<D>(vst, p[1], 1, st.acc_i);
+
+    if (t + 1 < nkb) {
+      const int nv1 = min(kBlock, a.N - (t + 1) * kBlock);
+      if (nv1 < kBlock) mask_scores(sn, nv1);
+      const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
+      const float m_new = fmaxf(st.m, step_max(sn, cp_next));
+      if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
+      st.m = m_new;
+      cp_cur = cp_next;
+    }
+    ld.store(kbuf + (t & 1) * C::KT, vbuf + ((t + 1) & 1) * C::VT, t + 2 < nkb, t + 1 < nkb);
     __syncthreads();
+  };
+  v16f s_alt[2];
+  int t = 0;
+  for (; t + 1 < nkb; t += 2) {
+    step(s_cur, s_alt, t);
+    step(s_alt, s_cur, t + 1);
   }
+  if (t < nkb) step(s_cur, s_alt, t);
 
   // o = A s_v / (16 L): the x16 of the widened V codes and the 1/15 of the
   // dequantized P cancel against the quantized row sum.
@@ -349,31 +452,31 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
   }
 }
 
-// Debug: the same per-step code for the 64 queries of one Q block, dumping
-// step kv_blk.  Two waves, single-buffered.
+// Debug: the same per-step building blocks for the 64 queries of one Q
+// block, in program order, dumping step kv_blk.  Two waves, one stage.
 template <int D>
 __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs t) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGE + 2 * C::ACCF];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::KT + C::VT + 2 * C::ACCF];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const int bh = t.bh;
   const int q0 = t.q_blk * kBlock + wave * 32;
-  v4i qop[C::KC];
+  v8i qop[C::QC];
   load_q<D>(a, bh, q0 + ln, hf, qop);
   const float cq = a.s_q[(size_t)bh * a.nblk + t.q_blk];
   State<D> st;
-  state_init<D>(st, reinterpret_cast<float*>(smem + C::STAGE + wave * C::ACCF));
+  state_init<D>(st, reinterpret_cast<float*>(smem + C::KT + C::VT + wave * C::ACCF));
   TileLoad<D, 128> ld;
   for (int kb = 0; kb <= t.kv_blk; ++kb) {
-    ld.fetch(a, bh, kb);
-    ld.store(smem);
+    ld.fetch(a, bh, kb, kb);
+    ld.store(smem, smem + C::KT, true, true);
     __syncthreads();
     const int nvalid = min(kBlock, a.N - kb * kBlock);
     const float sk = a.s_k[(size_t)bh * a.nblk + kb];
     if (kb == t.kv_blk)
-      tile_step<D, true>(smem, qop, cq, a.alpha_g, sk, nvalid, st, &t, wave);
+      tile_step<D, true>(smem, smem + C::KT, qop, cq, a.alpha_g, sk, nvalid, st, &t, wave);
     else
-      tile_step<D, false>(smem, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave);
+      tile_step<D, false>(smem, smem + C::KT, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave);
     __syncthreads();
   }
 }

@@ -91,6 +91,11 @@ __device__ __forceinline__ int quant_code(float x, float inv) {
   return (int)q;
 }
 
+// Sign-magnitude nibble of a code in [-7, 7].
+__device__ __forceinline__ uint32_t sign_mag(int c) {
+  return c < 0 ? (8u | (uint32_t)(-c)) : (uint32_t)c;
+}
+
 __device__ __forceinline__ float block_max_256(float v, float* red) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
         int i = half * 4 + bi;
         int ch = amax > 0.0f ? quant_code(y[16 * g + i], inv) : 0;
         int cl = amax > 0.0f ? quant_code(y[16 * g + i + 8], inv) : 0;
-        uint32_t byte = (((uint32_t)ch & 15u) << 4) | ((uint32_t)cl & 15u);
+        uint32_t byte = (sign_mag(ch) << 4) | sign_mag(cl);
         w |= byte << (8 * bi);
       }
       packed[2 * g + half] = w;
