@@ -22,8 +22,9 @@ constexpr int kWave = 64;
 // Exponent grid of the range-optimized P map: the exponent of p (in log2
 // units) is rounded to a multiple of 1/kPGrid.  On this grid no point other
 // than p = 1/2 comes within 3e-5 (relative) of a rounding boundary of 15 p,
-// so the hardware exp2 (error ~1e-7) decides every code exactly; an
-// exhaustive probe over all grid points checks it.
+// so the hardware exp2 (error ~1e-7) decides every code exactly.  The
+// kernels build their P-map table from that exp2 form; an exhaustive probe
+// over all grid points checks the table path.
 constexpr int kPGrid = 4755;
 constexpr float kInvPGrid = 1.0f / 4755.0f;
 constexpr float kLog2Of15 = (float)3.9068905956085187;
@@ -36,12 +37,14 @@ constexpr float kLog2Of15 = (float)3.9068905956085187;
 //     (bit 3 = sign, bits 0-2 = |code|; codes lie in [-7, 7]).
 //   * V tile of one 64-key block: for each channel d, 32 bytes holding the 64
 //     key slots in MFMA operand order, grouped by 16 slots like Q/K rows,
-//     nibbles in two's complement.
-//   Slot s = 32*ks + 16*hf + j carries key 32*ks + 8*(j/4) + 4*hf + (j%4):
-//   the key that the 32x32 MFMA accumulator of S^T = K Q^T leaves in
-//   register j of the lane half hf, so P feeds the PV MFMA with no shuffle.
-__host__ __device__ constexpr int slot_key_i8(int slot) {
-  return 32 * (slot >> 5) + 8 * ((slot & 15) >> 2) + 4 * ((slot >> 4) & 1) + (slot & 3);
+//     nibbles sign-magnitude like Q/K.
+//   Slot s = 32*hf + 16*mt + j (j < 16) carries key 32*mt + 8*(j/4) + 4*hf +
+//   (j%4): the key that the 32x32 accumulator of M-tile mt of S^T = K Q^T
+//   leaves in register j of lane half hf.  Lane half hf supplies K-elements
+//   32*hf..32*hf+31 of the PV MFMA's B operand, so the P codes of a lane are
+//   that operand as they stand, with no shuffle.
+__host__ __device__ constexpr int slot_key_pv(int slot) {
+  return 32 * ((slot >> 4) & 1) + 8 * ((slot & 15) >> 2) + 4 * (slot >> 5) + (slot & 3);
 }
 
 // bf16 path: 16-slot K-steps; slot s = 16*ks + 8*hf + j carries key
@@ -49,13 +52,6 @@ __host__ __device__ constexpr int slot_key_i8(int slot) {
 __host__ __device__ constexpr int slot_key_bf16(int slot) {
   return 32 * (slot >> 5) + 8 * (2 * ((slot >> 4) & 1) + ((slot & 7) >> 2)) +
          4 * ((slot >> 3) & 1) + (slot & 3);
-}
-
-// Widen 8 packed two's-complement nibble codes (one dword) to 16*code int8
-// values: high nibbles -> bytes of `hi`, low nibbles -> bytes of `lo`.
-__device__ __forceinline__ void unpack_x16(uint32_t w, uint32_t& hi, uint32_t& lo) {
-  hi = w & 0xF0F0F0F0u;
-  lo = (w << 4) & 0xF0F0F0F0u;
 }
 
 // Widen 8 packed sign-magnitude nibble codes to OCP fp8 e4m3 bytes (exact for

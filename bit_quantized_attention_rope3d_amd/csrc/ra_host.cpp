@@ -468,11 +468,7 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
       hipMemcpy(s_k, w + L.off_sk, BH * L.nblk * 4, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(s_v, w + L.off_sv, BH * D * 4, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(RA_ERR_HIP, "copy of prologue outputs failed");
-  auto nib = [](uint8_t byte, bool high) -> int8_t {     // two's complement (V)
-    int x = high ? (byte >> 4) : (byte & 15);
-    return (int8_t)(x >= 8 ? x - 16 : x);
-  };
-  auto nib_sm = [](uint8_t byte, bool high) -> int8_t {  // sign-magnitude (Q, K)
+  auto nib_sm = [](uint8_t byte, bool high) -> int8_t {  // sign-magnitude nibble
     int x = high ? (byte >> 4) : (byte & 15);
     return (int8_t)((x & 8) ? -(x & 7) : x);
   };
@@ -498,10 +494,10 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
         const uint8_t* r = pv.data() + ((bh * L.nkb + kb) * D + d) * 32;
         for (int sg = 0; sg < 4; ++sg)
           for (int i = 0; i < 8; ++i) {
-            const int key_hi = kb * 64 + ra::slot_key_i8(sg * 16 + i);
-            const int key_lo = kb * 64 + ra::slot_key_i8(sg * 16 + i + 8);
-            if (key_hi < N) v_codes[(bh * N + key_hi) * D + d] = nib(r[8 * sg + i], true);
-            if (key_lo < N) v_codes[(bh * N + key_lo) * D + d] = nib(r[8 * sg + i], false);
+            const int key_hi = kb * 64 + ra::slot_key_pv(sg * 16 + i);
+            const int key_lo = kb * 64 + ra::slot_key_pv(sg * 16 + i + 8);
+            if (key_hi < N) v_codes[(bh * N + key_hi) * D + d] = nib_sm(r[8 * sg + i], true);
+            if (key_lo < N) v_codes[(bh * N + key_lo) * D + d] = nib_sm(r[8 * sg + i], false);
           }
       }
   return ok();

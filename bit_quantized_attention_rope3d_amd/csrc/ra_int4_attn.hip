@@ -11,21 +11,26 @@
 //     one XCD walk the same head, sharing K/V tiles in that XCD's L2.
 //   * Per 64-key step the packed INT4 K and V tiles (4 KB + 4 KB for D = 128)
 //     are fetched with one 16-byte load per thread, widened once per
-//     workgroup to int8 (x16, a shift and two masks per 8 codes) into LDS
+//     workgroup to fp8 e4m3 (a v_perm table lookup per 4 codes) into LDS
 //     (XOR-swizzled rows, no padding), double-buffered, one barrier per step.
 //   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 with the INT4 codes widened to
 //     fp8 e4m3 (exact for |code| <= 7; every partial sum is an integer below
 //     2^24, so the fp32 accumulator holds the exact integer score and no
 //     int->float conversion is needed).  Each lane holds one query column, so
 //     row max / row sum are in-lane (+1 cross-half swap).
-//   * P codes come straight out of the accumulator registers as bytes
-//     (exponent FMA, round, exp2, cvt_pk_u8) in the order the PV MFMA wants
-//     them as its B operand; V is stored pre-permuted to match.
-//   * PV accumulates u * vhat in INT32 registers across steps; the fp32
-//     accumulator lives in LDS (16 KB per wave) and is touched only when some
-//     row's running max rises (then A = (A + I) * beta), which is rare after
-//     the first few steps.  This keeps a wave within 256 VGPRs, i.e. two
-//     waves per SIMD.
+//   * P codes come straight out of the accumulator registers: the distance
+//     of each score below the running max, rounded to the exponent grid, is
+//     turned into an index with one FMA, one add and one saturating subtract
+//     and looked up in a 46 KB table of 16-bit entries in LDS (u as e4m3 for
+//     the MFMA in the low byte, u as an integer for the row sum in the high
+//     byte), built per workgroup from the exp2 form of the map.  The e4m3
+//     bytes are packed in the order the PV MFMA wants them as its B operand;
+//     V is stored pre-permuted to match.
+//   * PV = V^T P^T also runs on the fp8 MFMA: u in [0, 15] and the V codes
+//     are exact in e4m3 and a step's sums are integers below 2^24, so each
+//     step's PV is exact; it accumulates across steps in fp32 registers,
+//     scaled by beta only when a query's running max rises (rare after the
+//     first few steps).  A wave stays within 256 VGPRs (two waves per SIMD).
 #include "ra_common.h"
 #include "ra_kernels.h"
 
@@ -40,7 +45,6 @@ struct Cfg {
   static constexpr int KPARTS = D / 32;    // 16-byte packed parts per key row
   static constexpr int KP = 64 * KPARTS;   // packed K parts per tile
   static constexpr int TOT = KP + 2 * D;   // + packed V parts (2 per channel)
-  static constexpr int ACCF = DT * 4 * 64 * 16;   // LDS bytes of one wave's fp32 accumulator
 };
 
 // LDS rows are XOR-swizzled in 16-byte chunks.  The gfx950 LDS serves a
@@ -57,12 +61,61 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 template <int D>
 struct State {
-  v16i acc_i[Cfg<D>::DT];   // INT32 sum of u * (16 vhat) since the last rescale
+  v16f acc[Cfg<D>::DT];     // O^T: sum of u * vhat, scaled by beta when m rises
   float m;                  // running max (grid units), this lane's query
   float L;                  // fp32 part of the row sum
   uint32_t U;               // integer row sum of u since the last rescale (lane half)
-  float* accf;              // this wave's fp32 accumulator in LDS: [DT*4][64 lanes][4]
 };
+
+// ---- range-optimized P map through an LDS byte table ----------------------
+//
+// For a score S with scale c and running max m (grid units), the grid
+// exponent is x = rint(f32(S c - m)) <= 0 and the code is u(x).  With
+// n = -x = rint(f32(m - S c)) (rounding is symmetric), the table holds
+// tab[i] = u(i - kPTabMax) for i <= kPTabMax and the index is
+// max(kPTabMax - n, 0): u vanishes for n >= kPTabMax.
+//   v = fma(S, -c, m)            f32(m - S c) >= 0, since m >= max S c
+//   w = v + 1.5 * 2^23           for v < 2^22: exactly 1.5*2^23 + rint(v)
+//                                (the add rounds to nearest even at unit
+//                                 spacing); larger, +inf and NaN land above
+//   i = sat(bits(1.5*2^23) + kPTabMax - bits(w))   unsigned saturating
+constexpr int kPTabMax = 23333;              // u(x) = 0 for x <= -kPTabMax
+constexpr int kPTabEntries = 23552;          // 16-bit entries (>= kPTabMax + 1)
+constexpr int kPTabBytes = 2 * kPTabEntries;
+constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
+constexpr uint32_t kPTabBase = 0x4B400000u + (uint32_t)kPTabMax;
+
+__device__ __forceinline__ uint32_t ptab_index(float s, float c, float m) {
+  const float v = __builtin_fmaf(s, -c, m);
+  const float w = v + kRoundMagic;
+  return __builtin_elementwise_sub_sat(kPTabBase, __float_as_uint(w));
+}
+
+// e4m3 encoding of an integer 0 <= u <= 15 (exact).
+__device__ __forceinline__ uint32_t e4m3_of_uint(uint32_t u) {
+  if (u == 0u) return 0u;
+  const uint32_t e = 31u - (uint32_t)__builtin_clz(u);       // floor(log2 u) <= 3
+  return ((e + 7u) << 3) | ((u << (3u - e)) & 7u);
+}
+
+// Inverse of e4m3_of_uint (debug dumps).
+__device__ __forceinline__ uint32_t e4m3_to_uint(uint32_t b) {
+  if (b == 0u) return 0u;
+  const uint32_t e = (b >> 3) - 7u, m = b & 7u;
+  return ((8u | m) << e) >> 3;
+}
+
+// Fill the table cooperatively (threads tid, tid + nt, ...) from the exp2
+// form of the map, exact on every grid point: entry i = e4m3(u) | u << 8 for
+// u = u(i - kPTabMax).  Entries past kPTabMax are never indexed by a valid
+// running max; they hold u(0).
+__device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt) {
+  for (int i = tid; i < kPTabEntries; i += nt) {
+    const float x = (float)(min(i, kPTabMax) - kPTabMax);
+    const uint32_t u = pmap_insert(x, 0u, 0u) & 0xFFu;
+    reinterpret_cast<uint16_t*>(tab)[i] = (uint16_t)(e4m3_of_uint(u) | (u << 8));
+  }
+}
 
 // Cooperative fetch of packed tiles into registers and widening store into
 // LDS.  The K part and the V part may belong to different key steps (the
@@ -73,18 +126,26 @@ struct TileLoad {
   static constexpr bool EXACT = Cfg<D>::TOT % NT == 0;
   v4u r[NP];
 
+  // Part p = threadIdx.x + i * NT.  KP and NT are multiples of 64, so whether
+  // a part is K or V is decided per wave; deriving it from the wave index
+  // (an SGPR) makes it a scalar branch rather than per-lane selects.
+  __device__ __forceinline__ static int wave_base(int i) {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u)) + i * NT;
+  }
+
   __device__ __forceinline__ void fetch(const AttnArgs& a, int bh, int kt, int vt) {
     using C = Cfg<D>;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int p = threadIdx.x + i * NT;
+      const int pb = wave_base(i);
+      const int p = pb + (threadIdx.x & 63);
       const int pv = p - C::KP;
-      const bool isk = p < C::KP;
+      const bool isk = pb < C::KP;
       const int t = isk ? kt : vt;
       const uint8_t* src = isk
           ? a.kp + ((size_t)bh * a.Npad + (size_t)kt * kBlock + p / C::KPARTS) * (D / 2) + (p % C::KPARTS) * 16
           : a.vp + (((size_t)bh * a.nkb + vt) * D + (pv >> 1)) * 32 + (pv & 1) * 16;
-      if ((EXACT || p < C::TOT) && t >= 0) r[i] = *reinterpret_cast<const v4u*>(src);
+      if ((EXACT || pb < C::TOT) && t >= 0) r[i] = *reinterpret_cast<const v4u*>(src);
     }
   }
 
@@ -92,10 +153,11 @@ struct TileLoad {
     using C = Cfg<D>;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int p = threadIdx.x + i * NT;
-      if (!EXACT && p >= C::TOT) continue;
+      const int pb = wave_base(i);
+      const int p = pb + (threadIdx.x & 63);
+      if (!EXACT && pb >= C::TOT) continue;
       const int pv = p - C::KP;
-      const bool isk = p < C::KP;
+      const bool isk = pb < C::KP;
       if (isk ? !do_k : !do_v) continue;
       const int row = isk ? p / C::KPARTS : (pv >> 1);
       const int c0 = 2 * (isk ? p % C::KPARTS : (pv & 1));
@@ -105,11 +167,11 @@ struct TileLoad {
         unpack_e4m3(r[i][1], h1, l1);
         unpack_e4m3(r[i][2], h2, l2);
         unpack_e4m3(r[i][3], h3, l3);
-      } else {              // V codes -> 16 * code int8 (PV runs on the i8 MFMA)
-        unpack_x16(r[i][0], h0, l0);
-        unpack_x16(r[i][1], h1, l1);
-        unpack_x16(r[i][2], h2, l2);
-        unpack_x16(r[i][3], h3, l3);
+      } else {              // V codes -> fp8 e4m3 as well (PV runs on the fp8 MFMA)
+        unpack_e4m3(r[i][0], h0, l0);
+        unpack_e4m3(r[i][1], h1, l1);
+        unpack_e4m3(r[i][2], h2, l2);
+        unpack_e4m3(r[i][3], h3, l3);
       }
       uint8_t* base = isk ? kst : vst;
       const int o0 = isk ? swz<D>(row, c0) : swz<64>(row, c0);
@@ -165,7 +227,16 @@ __device__ __forceinline__ void qk_step(const uint8_t* kst, const v8i (&qop)[Cfg
   }
 }
 
-// Keys at or past `nvalid` (ragged last step) are excluded from the max.
+// Keys at or past `nvalid` (ragged last step) get S = -inf: they drop out of
+// the max and map to u = 0.  The mask runs only on the ragged last key step;
+// its argument is passed through opaque_sgpr() so that the compiler can
+// neither hoist the 32 key comparisons out of that branch nor if-convert the
+// masking into selects executed on every step.
+__device__ __forceinline__ int opaque_sgpr(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 __device__ __forceinline__ void mask_scores(v16f (&s)[2], int nvalid) {
   const int hf = (threadIdx.x & 63) >> 5;
 #pragma unroll
@@ -187,68 +258,51 @@ __device__ __forceinline__ float step_max(const v16f (&s)[2], float c) {
   return mul_round_up(mx, c);
 }
 
-// P codes of M-tile mt (u = code + 8) as the 16-byte B operand of the PV MFMA.
-__device__ __forceinline__ void pmap_mtile(const v16f& s, float c, float m, uint32_t (&p)[4]) {
+// P codes of M-tile mt (u = code + 8) as e4m3 bytes, half of the 32-byte B
+// operand of the PV MFMA: register 4i+e of the tile goes to byte e of word
+// i.  U accumulates the integer u (v_sad_u8 over the four high bytes).  Keys
+// masked to S = -inf give v = +inf (or NaN when c = 0) and thus u = 0.
+__device__ __forceinline__ void pmap_mtile(const v16f& s, float c, float m, const uint8_t* tab,
+                                           uint32_t (&p)[4], uint32_t& U) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t acc = 0u;
+    uint32_t b[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float dlt = __builtin_fmaf(s[4 * i + e], c, -m);
-      const float x = __builtin_rintf(dlt);
-      acc = pmap_insert(x, (uint32_t)e, acc);
-    }
-    p[i] = acc;
+    for (int e = 0; e < 4; ++e) b[e] = reinterpret_cast<const uint16_t*>(tab)[ptab_index(s[4 * i + e], c, m)];
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x05010400u);   // e0 e1 u0 u1
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x05010400u);   // e2 e3 u2 u3
+    p[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    U = __builtin_amdgcn_sad_u8(__builtin_amdgcn_perm(hi, lo, 0x07060302u), 0u, U);
   }
 }
 
-__device__ __forceinline__ void mask_codes(uint32_t (&p)[2][4], int nvalid) {
-  const int hf = (threadIdx.x & 63) >> 5;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (acc_key(mt, r, hf) >= nvalid) p[mt][r >> 2] &= ~(0xFFu << (8 * (r & 3)));
-}
-
-__device__ __forceinline__ uint32_t code_sum(const uint32_t (&p)[4], uint32_t U) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) U = __builtin_amdgcn_sad_u8(p[i], 0u, U);
-  return U;
-}
-
-// O^T += V^T P^T for K-step ks (keys 32ks..32ks+31) of the step.
+// O^T += V^T P^T over the 64 keys of the step: lane half hf supplies slots
+// 32hf..32hf+31, i.e. 16-byte chunks 2hf and 2hf+1 of each V row.
 template <int D>
-__device__ __forceinline__ void pv_kstep(const uint8_t* vst, const uint32_t (&p)[4], int ks,
-                                         v16i (&acc)[Cfg<D>::DT]) {
+__device__ __forceinline__ void pv_step(const uint8_t* vst, const uint32_t (&p)[2][4],
+                                        v16f (&acc)[Cfg<D>::DT]) {
   const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
-  const v4i pb = v4i{(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
+  const v8i pb = v8i{(int)p[0][0], (int)p[0][1], (int)p[0][2], (int)p[0][3],
+                     (int)p[1][0], (int)p[1][1], (int)p[1][2], (int)p[1][3]};
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
-    const v4i va = *reinterpret_cast<const v4i*>(vst + swz<64>(dt * 32 + ln, ks * 2 + hf));
-    acc[dt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, pb, acc[dt], 0, 0, 0);
+    const int row = dt * 32 + ln;
+    const v4i v0 = *reinterpret_cast<const v4i*>(vst + swz<64>(row, 2 * hf));
+    const v4i v1 = *reinterpret_cast<const v4i*>(vst + swz<64>(row, 2 * hf + 1));
+    const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[dt], 0, 0, 0, 0, 0, 0);
   }
 }
 
-// The running max rises from st.m to m_new: fold the integer accumulator into
-// the fp32 one with the rescale, A = (A + I) * beta, L = (L + U) * beta.
+// The running max rises from st.m to m_new: A = A * beta, L = (L + U) * beta.
+// beta = 0 on the first step (st.m = -inf).
 template <int D>
 __device__ __forceinline__ void rescale(State<D>& st, float m_new) {
-  const int lane = threadIdx.x & 63;
   const float beta = exp2f((st.m - m_new) * kInvPGrid);
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      v4f* pa = reinterpret_cast<v4f*>(st.accf) + (dt * 4 + g) * 64 + lane;
-      v4f acc = *pa;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] = (acc[e] + (float)st.acc_i[dt][4 * g + e]) * beta;
-        st.acc_i[dt][4 * g + e] = 0;
-      }
-      *pa = acc;
-    }
+    for (int r = 0; r < 16; ++r) st.acc[dt][r] *= beta;
   st.L = (st.L + (float)st.U) * beta;
   st.U = 0u;
 }
@@ -262,7 +316,7 @@ __device__ __forceinline__ float score_scale(float cq, float sk, float alpha_g) 
 // One whole 64-key step in program order (used by the parity dump kernel;
 // the main kernel runs the same blocks software-pipelined).
 template <int D, bool DUMP>
-__device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst,
+__device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst, const uint8_t* tab,
                                           const v8i (&qop)[Cfg<D>::QC], float cq, float alpha_g,
                                           float sk, int nvalid, State<D>& st,
                                           const TileDumpArgs* dump, int wave) {
@@ -276,19 +330,15 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
   if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
   st.m = m_new;
   uint32_t p[2][4];
-  pmap_mtile(s[0], cp, m_new, p[0]);
-  pmap_mtile(s[1], cp, m_new, p[1]);
-  if (nvalid < kBlock) mask_codes(p, nvalid);
-  st.U = code_sum(p[0], st.U);
-  st.U = code_sum(p[1], st.U);
-  pv_kstep<D>(vst, p[0], 0, st.acc_i);
-  pv_kstep<D>(vst, p[1], 1, st.acc_i);
+  pmap_mtile(s[0], cp, m_new, tab, p[0], st.U);
+  pmap_mtile(s[1], cp, m_new, tab, p[1], st.U);
+  pv_step<D>(vst, p, st.acc);
 
   if (DUMP) {
-    // Exact per-step integers: S, P codes, PV = sum (u - 8) vhat, running max.
+    // Exact per-step integers: S, P codes (decoded from the e4m3 operand
+    // bytes), PV = sum (u - 8) vhat = sum u vhat - 8 sum vhat, running max.
     const int qrow = wave * 32 + ln;
-    const v16i z = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    v16i pv[C::DT], cs[C::DT];
+    v16f pv[C::DT], cs[C::DT];
     uint32_t ones[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -296,52 +346,48 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
       for (int r = 0; r < 16; ++r) {
         const int key = acc_key(mt, r, hf);
         if (r % 4 == 0) ones[mt][r >> 2] = 0u;
-        if (key < nvalid) ones[mt][r >> 2] |= 1u << (8 * (r & 3));
+        if (key < nvalid) ones[mt][r >> 2] |= 0x38u << (8 * (r & 3));   // e4m3 1.0
         const int sv = key < nvalid ? (int)s[mt][r] : 0;
-        const int code = (int)((p[mt][r >> 2] >> (8 * (r & 3))) & 0xFFu) - 8;
+        const int code = (int)e4m3_to_uint((p[mt][r >> 2] >> (8 * (r & 3))) & 0xFFu) - 8;
         dump->s_int[qrow * 64 + key] = sv;
         dump->p_code[qrow * 64 + key] = (int8_t)code;
       }
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) { pv[dt] = z; cs[dt] = z; }
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      pv_kstep<D>(vst, p[ks], ks, pv);
-      pv_kstep<D>(vst, ones[ks], ks, cs);
-    }
+      for (int r = 0; r < 16; ++r) { pv[dt][r] = 0.0f; cs[dt][r] = 0.0f; }
+    pv_step<D>(vst, p, pv);
+    pv_step<D>(vst, ones, cs);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int d = dt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        dump->pv_int[qrow * D + d] = (pv[dt][r] - 8 * cs[dt][r]) / 16;
+        dump->pv_int[qrow * D + d] = (int)pv[dt][r] - 8 * (int)cs[dt][r];
       }
     if (hf == 0) dump->m_after[qrow] = st.m;
   }
 }
 
 template <int D>
-__device__ __forceinline__ void state_init(State<D>& st, float* accf) {
+__device__ __forceinline__ void state_init(State<D>& st) {
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.acc_i[dt][r] = 0;
+    for (int r = 0; r < 16; ++r) st.acc[dt][r] = 0.0f;
   st.m = -INFINITY;
   st.L = 0.0f;
   st.U = 0u;
-  st.accf = accf;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < Cfg<D>::DT * 4; ++i)
-    reinterpret_cast<v4f*>(accf)[i * 64 + lane] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::KT + 2 * C::VT + 8 * C::ACCF];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::KT + 2 * C::VT + kPTabBytes];
   uint8_t* const kbuf = smem;                     // 2 K stages
   uint8_t* const vbuf = smem + 2 * C::KT;         // 2 V stages
+  uint8_t* const ptab = smem + 2 * C::KT + 2 * C::VT;
+  ptab_build(ptab, threadIdx.x, 512);             // visible after the first barrier
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of (head, query-tile) ids.
@@ -361,69 +407,69 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
   const float* sk = a.s_k + (size_t)bh * a.nblk;
 
   State<D> st;
-  state_init<D>(st, reinterpret_cast<float*>(smem + 2 * C::KT + 2 * C::VT + wave * C::ACCF));
+  state_init<D>(st);
 
   // Pipeline: during step t the wave computes S of step t+1 (K one stage
   // ahead) while it turns S of step t into P codes, then P x V of step t;
-  // one barrier per step.  K of step t+2 and V of step t+1 are fetched
-  // during step t and widened into the stages freed by step t-1.
-  TileLoad<D, 512> ld;
-  ld.fetch(a, bh, 0, -1);
-  ld.store(kbuf, vbuf, true, false);
+  // one barrier per step.  At the end of step t, K of step t+2 and V of step
+  // t+1 are widened into the LDS stages freed by step t-1; their global
+  // loads were issued at the start of step t-1 into one of two register
+  // sets, so each load has a whole step to arrive.
+  TileLoad<D, 512> ldA, ldB;
+  ldA.fetch(a, bh, 0, -1);
+  ldA.store(kbuf, vbuf, true, false);
   __syncthreads();
-  ld.fetch(a, bh, nkb > 1 ? 1 : -1, 0);
+  ldA.fetch(a, bh, nkb > 1 ? 1 : -1, 0);
+  ldB.fetch(a, bh, nkb > 2 ? 2 : -1, nkb > 1 ? 1 : -1);
   v16f s_cur[2];
   qk_step<D>(kbuf, qop, s_cur);
   const int nv0 = min(kBlock, a.N);
   if (nv0 < kBlock) mask_scores(s_cur, nv0);
   float cp_cur = score_scale(cq, sk[0], a.alpha_g);
   st.m = step_max(s_cur, cp_cur);
-  ld.store(kbuf + C::KT, vbuf, nkb > 1, true);
+  ldA.store(kbuf + C::KT, vbuf, nkb > 1, true);
   __syncthreads();
 
-  // One pipelined step; the two score register sets swap roles every step
-  // (the loop is unrolled by two so that no copy is needed).
-  auto step = [&](v16f (&sc)[2], v16f (&sn)[2], int t) {
-    ld.fetch(a, bh, t + 2 < nkb ? t + 2 : -1, t + 1 < nkb ? t + 1 : -1);
+  // One pipelined step; the score register sets and the staging register
+  // sets swap roles every step (the loop is unrolled by two so that no copy
+  // is needed).  lx holds K t+2 / V t+1, ly receives K t+3 / V t+2.
+  auto step = [&](v16f (&sc)[2], v16f (&sn)[2], TileLoad<D, 512>& lx, TileLoad<D, 512>& ly,
+                  int t) {
+    ly.fetch(a, bh, t + 3 < nkb ? t + 3 : -1, t + 2 < nkb ? t + 2 : -1);
     const uint8_t* kst = kbuf + ((t + 1) & 1) * C::KT;
     const uint8_t* vst = vbuf + (t & 1) * C::VT;
 
     qk_step<D>(kst, qop, sn);                     // S of step t+1 (unused after the last step)
     uint32_t p[2][4];
-    pmap_mtile(sc[0], cp_cur, st.m, p[0]);
-    pmap_mtile(sc[1], cp_cur, st.m, p[1]);
-    const int nvalid = min(kBlock, a.N - t * kBlock);
-    if (nvalid < kBlock) mask_codes(p, nvalid);
-    st.U = code_sum(p[0], st.U);
-    st.U = code_sum(p[1], st.U);
-    pv_kstep<D>(vst, p[0], 0, st.acc_i);
-    pv_kstep<D>(vst, p[1], 1, st.acc_i);
+    pmap_mtile(sc[0], cp_cur, st.m, ptab, p[0], st.U);
+    pmap_mtile(sc[1], cp_cur, st.m, ptab, p[1], st.U);
+    pv_step<D>(vst, p, st.acc);
 
     if (t + 1 < nkb) {
       const int nv1 = min(kBlock, a.N - (t + 1) * kBlock);
-      if (nv1 < kBlock) mask_scores(sn, nv1);
+      if (nv1 < kBlock) mask_scores(sn, opaque_sgpr(nv1));
       const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
       const float m_new = fmaxf(st.m, step_max(sn, cp_next));
       if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
       st.m = m_new;
       cp_cur = cp_next;
     }
-    ld.store(kbuf + (t & 1) * C::KT, vbuf + ((t + 1) & 1) * C::VT, t + 2 < nkb, t + 1 < nkb);
+    lx.store(kbuf + (t & 1) * C::KT, vbuf + ((t + 1) & 1) * C::VT, t + 2 < nkb, t + 1 < nkb);
     __syncthreads();
   };
   v16f s_alt[2];
   int t = 0;
   for (; t + 1 < nkb; t += 2) {
-    step(s_cur, s_alt, t);
-    step(s_alt, s_cur, t + 1);
+    step(s_cur, s_alt, ldB, ldA, t);
+    step(s_alt, s_cur, ldA, ldB, t + 1);
   }
-  if (t < nkb) step(s_cur, s_alt, t);
+  if (t < nkb) step(s_cur, s_alt, ldB, ldA, t);
 
-  // o = A s_v / (16 L): the x16 of the widened V codes and the 1/15 of the
-  // dequantized P cancel against the quantized row sum.
+  // o = A s_v / L: the 1/15 of the dequantized P cancels against the
+  // quantized row sum.
   const float lw = st.L + (float)st.U;
   const float lt = xhalf_sum_f(lw);
-  const float inv = 1.0f / (16.0f * lt);
+  const float inv = 1.0f / lt;
   const int q = q0 + ln;
   if (q < a.N) {
     const int b = bh / a.H, h = bh % a.H;
@@ -434,11 +480,10 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int d = dt * 32 + 8 * g + 4 * hf;
         const v4f sv = *reinterpret_cast<const v4f*>(a.s_v + (size_t)bh * D + d);
-        const v4f af = reinterpret_cast<const v4f*>(st.accf)[(dt * 4 + g) * 64 + lane];
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          o[e] = (af[e] + (float)st.acc_i[dt][4 * g + e]) * sv[e] * inv;
+          o[e] = st.acc[dt][4 * g + e] * sv[e] * inv;
         if (OUT_BF16) {
           uint16_t* op = static_cast<uint16_t*>(a.out) + obase + d;
           *reinterpret_cast<uint2*>(op) =
@@ -457,7 +502,9 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs t) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::KT + C::VT + 2 * C::ACCF];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::KT + C::VT + kPTabBytes];
+  uint8_t* const ptab = smem + C::KT + C::VT;
+  ptab_build(ptab, threadIdx.x, 128);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const int bh = t.bh;
   const int q0 = t.q_blk * kBlock + wave * 32;
@@ -465,7 +512,7 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   load_q<D>(a, bh, q0 + ln, hf, qop);
   const float cq = a.s_q[(size_t)bh * a.nblk + t.q_blk];
   State<D> st;
-  state_init<D>(st, reinterpret_cast<float*>(smem + C::KT + C::VT + wave * C::ACCF));
+  state_init<D>(st);
   TileLoad<D, 128> ld;
   for (int kb = 0; kb <= t.kv_blk; ++kb) {
     ld.fetch(a, bh, kb, kb);
@@ -474,16 +521,23 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
     const int nvalid = min(kBlock, a.N - kb * kBlock);
     const float sk = a.s_k[(size_t)bh * a.nblk + kb];
     if (kb == t.kv_blk)
-      tile_step<D, true>(smem, smem + C::KT, qop, cq, a.alpha_g, sk, nvalid, st, &t, wave);
+      tile_step<D, true>(smem, smem + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, &t, wave);
     else
-      tile_step<D, false>(smem, smem + C::KT, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave);
+      tile_step<D, false>(smem, smem + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave);
     __syncthreads();
   }
 }
 
-__global__ void k_pmap_probe(const float* __restrict__ x, uint8_t* __restrict__ u, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) u[i] = (uint8_t)(pmap_insert(x[i], 0u, 0u) & 0xFFu);
+// The kernels' P map on grid exponents x <= 0: the same table and index
+// arithmetic, with S = x, c = 1, m = 0 (so v = -x exactly).
+__global__ __launch_bounds__(256) void k_pmap_probe(const float* __restrict__ x, uint8_t* __restrict__ u,
+                                                    int64_t n) {
+  __shared__ __attribute__((aligned(16))) uint8_t tab[kPTabBytes];
+  ptab_build(tab, threadIdx.x, 256);
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    u[i] = (uint8_t)(reinterpret_cast<const uint16_t*>(tab)[ptab_index(x[i], 1.0f, 0.0f)] >> 8);
 }
 
 __global__ void k_copy16(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n16) {
@@ -515,7 +569,8 @@ void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipS
 
 void launch_pmap_probe(const float* x, uint8_t* u, int64_t n, hipStream_t st) {
   if (n <= 0) return;
-  k_pmap_probe<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, u, n);
+  const int64_t blocks = (n + 255) / 256;
+  k_pmap_probe<<<(unsigned)(blocks < 1024 ? blocks : 1024), 256, 0, st>>>(x, u, n);
 }
 
 void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {

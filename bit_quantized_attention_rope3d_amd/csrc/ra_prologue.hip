@@ -248,10 +248,10 @@ __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         int i = half * 4 + bi;
-        int kh = slot_key_i8(sg * 16 + i), kl = slot_key_i8(sg * 16 + i + 8);
+        int kh = slot_key_pv(sg * 16 + i), kl = slot_key_pv(sg * 16 + i + 8);
         int ch = amax > 0.0f ? quant_code(tile[kh][d], inv) : 0;
         int cl = amax > 0.0f ? quant_code(tile[kl][d], inv) : 0;
-        acc |= ((((uint32_t)ch & 15u) << 4) | ((uint32_t)cl & 15u)) << (8 * bi);
+        acc |= ((sign_mag(ch) << 4) | sign_mag(cl)) << (8 * bi);
       }
       w[half] = acc;
     }
