@@ -29,15 +29,14 @@ constexpr int kPGrid = 4755;
 constexpr float kInvPGrid = 1.0f / 4755.0f;
 constexpr float kLog2Of15 = (float)3.9068905956085187;
 
-// Packed INT4 layout, shared by the prologue (writer) and the attention
-// kernels (readers):
-//   * Q/K rows: D/2 bytes per token; 16-channel group g occupies bytes
-//     8g..8g+7, byte i of a group holds channel 16g+i in its high nibble and
-//     channel 16g+i+8 in its low nibble.  Nibbles are sign-magnitude
-//     (bit 3 = sign, bits 0-2 = |code|; codes lie in [-7, 7]).
-//   * V tile of one 64-key block: for each channel d, 32 bytes holding the 64
-//     key slots in MFMA operand order, grouped by 16 slots like Q/K rows,
-//     nibbles sign-magnitude like Q/K.
+// Code layout in the workspace, shared by the prologue (writer) and the
+// attention kernels (readers).  Every INT4 code (Q, K, V in [-7, 7]) is
+// stored as one byte holding its fp8 e4m3 encoding, which is exact: gfx950
+// has no INT4 matrix instruction, so the codes are widened to the 8-bit
+// MFMA operand format once here, not in each query tile of the attention.
+//   * Q/K rows: D bytes per token in channel order.
+//   * V tile of one 64-key block: for each channel d, 64 bytes holding the
+//     64 key slots in MFMA operand order.
 //   Slot s = 32*hf + 16*mt + j (j < 16) carries key 32*mt + 8*(j/4) + 4*hf +
 //   (j%4): the key that the 32x32 accumulator of M-tile mt of S^T = K Q^T
 //   leaves in register j of lane half hf.  Lane half hf supplies K-elements
@@ -54,15 +53,10 @@ __host__ __device__ constexpr int slot_key_bf16(int slot) {
          4 * ((slot >> 3) & 1) + (slot & 3);
 }
 
-// Widen 8 packed sign-magnitude nibble codes to OCP fp8 e4m3 bytes (exact for
-// |code| <= 7): the magnitude indexes a byte table with v_perm, the sign bit
-// moves to bit 7.  e4m3 of 0..7 = 00 38 40 44 48 4A 4C 4E.
-__device__ __forceinline__ void unpack_e4m3(uint32_t w, uint32_t& hi, uint32_t& lo) {
-  const uint32_t t_lo = 0x44403800u, t_hi = 0x4E4C4A48u;
-  const uint32_t mh = (w >> 4) & 0x07070707u;
-  const uint32_t ml = w & 0x07070707u;
-  hi = (w & 0x80808080u) | __builtin_amdgcn_perm(t_hi, t_lo, mh);
-  lo = ((w << 4) & 0x80808080u) | __builtin_amdgcn_perm(t_hi, t_lo, ml);
+// OCP fp8 e4m3 byte of an integer code c in [-7, 7] (exact): sign in bit 7,
+// |c| = 0..7 -> 00 38 40 44 48 4A 4C 4E.
+__host__ __device__ constexpr uint32_t e4m3_of_code(int c) {
+  return (c < 0 ? 0x80u : 0u) | (uint32_t)((0x4E4C4A4844403800ull >> (8 * (c < 0 ? -c : c))) & 0xFFu);
 }
 
 // Range-optimized P code, as u = code + 8 in [0, 15], of the grid exponent

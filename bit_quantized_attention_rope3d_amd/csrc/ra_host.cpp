@@ -8,6 +8,7 @@
 // merged into RoPE), Sec. 4.2 (P map), Sec. 5.1 (FP16 step/block fallback).
 #include "ra_attn.h"
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -103,7 +104,7 @@ Layout layout_of(const ra_shape* s, const ra_opts* o) {
   const size_t A = 256;
   size_t off = 0;
   if (o->prec == RA_PREC_INT4) {
-    const size_t tens = BH * L.Npad * D / 2;
+    const size_t tens = BH * L.Npad * D;     // one e4m3 byte per code
     L.off_q = off; off = align_up(off + tens, A);
     L.off_k = off; off = align_up(off + tens, A);
     L.off_v = off; off = align_up(off + tens, A);
@@ -458,7 +459,7 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
   const Layout& L = p->lay;
   const size_t BH = (size_t)p->shape.batch * p->shape.heads;
   const int D = p->shape.head_dim, N = L.N;
-  const size_t tens = BH * L.Npad * D / 2;
+  const size_t tens = BH * L.Npad * D;
   std::vector<uint8_t> pq(tens), pk(tens), pv(tens);
   const uint8_t* w = static_cast<const uint8_t*>(ws);
   if (hipMemcpy(pq.data(), w + L.off_q, tens, hipMemcpyDeviceToHost) != hipSuccess ||
@@ -468,37 +469,31 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
       hipMemcpy(s_k, w + L.off_sk, BH * L.nblk * 4, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(s_v, w + L.off_sv, BH * D * 4, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(RA_ERR_HIP, "copy of prologue outputs failed");
-  auto nib_sm = [](uint8_t byte, bool high) -> int8_t {  // sign-magnitude nibble
-    int x = high ? (byte >> 4) : (byte & 15);
-    return (int8_t)((x & 8) ? -(x & 7) : x);
-  };
-  // Q/K rows: group g of 16 channels, byte i -> channel 16g+i (high), 16g+i+8 (low).
+  // e4m3 byte -> code; bytes that encode no code in [-7, 7] decode to -128,
+  // which no valid code equals.
+  int8_t code_of[256];
+  for (int i = 0; i < 256; ++i) code_of[i] = INT8_MIN;
+  for (int c = -7; c <= 7; ++c) code_of[ra::e4m3_of_code(c)] = (int8_t)c;
   for (size_t bh = 0; bh < BH; ++bh)
     for (int n = 0; n < N; ++n) {
-      const uint8_t* rq = pq.data() + (bh * L.Npad + n) * (D / 2);
-      const uint8_t* rk = pk.data() + (bh * L.Npad + n) * (D / 2);
+      const uint8_t* rq = pq.data() + (bh * L.Npad + n) * D;
+      const uint8_t* rk = pk.data() + (bh * L.Npad + n) * D;
       int8_t* oq = q_codes + (bh * N + n) * D;
       int8_t* ok_ = k_codes + (bh * N + n) * D;
-      for (int g = 0; g < D / 16; ++g)
-        for (int i = 0; i < 8; ++i) {
-          oq[16 * g + i] = nib_sm(rq[8 * g + i], true);
-          oq[16 * g + i + 8] = nib_sm(rq[8 * g + i], false);
-          ok_[16 * g + i] = nib_sm(rk[8 * g + i], true);
-          ok_[16 * g + i + 8] = nib_sm(rk[8 * g + i], false);
-        }
+      for (int d = 0; d < D; ++d) {
+        oq[d] = code_of[rq[d]];
+        ok_[d] = code_of[rk[d]];
+      }
     }
   // V: per 64-key block and channel, 64 slots in operand order.
   for (size_t bh = 0; bh < BH; ++bh)
     for (int kb = 0; kb < L.nkb; ++kb)
       for (int d = 0; d < D; ++d) {
-        const uint8_t* r = pv.data() + ((bh * L.nkb + kb) * D + d) * 32;
-        for (int sg = 0; sg < 4; ++sg)
-          for (int i = 0; i < 8; ++i) {
-            const int key_hi = kb * 64 + ra::slot_key_pv(sg * 16 + i);
-            const int key_lo = kb * 64 + ra::slot_key_pv(sg * 16 + i + 8);
-            if (key_hi < N) v_codes[(bh * N + key_hi) * D + d] = nib_sm(r[8 * sg + i], true);
-            if (key_lo < N) v_codes[(bh * N + key_lo) * D + d] = nib_sm(r[8 * sg + i], false);
-          }
+        const uint8_t* r = pv.data() + ((bh * L.nkb + kb) * D + d) * 64;
+        for (int slot = 0; slot < 64; ++slot) {
+          const int key = kb * 64 + ra::slot_key_pv(slot);
+          if (key < N) v_codes[(bh * N + key) * D + d] = code_of[r[slot]];
+        }
       }
   return ok();
 }

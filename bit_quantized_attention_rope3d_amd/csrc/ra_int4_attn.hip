@@ -9,10 +9,11 @@
 //   * One workgroup = 8 waves = 256 query rows of one (b, h); each wave owns 32
 //     queries.  Workgroup ids are remapped so that the workgroups resident on
 //     one XCD walk the same head, sharing K/V tiles in that XCD's L2.
-//   * Per 64-key step the packed INT4 K and V tiles (4 KB + 4 KB for D = 128)
-//     are fetched with one 16-byte load per thread, widened once per
-//     workgroup to fp8 e4m3 (a v_perm table lookup per 4 codes) into LDS
-//     (XOR-swizzled rows, no padding), double-buffered, one barrier per step.
+//   * Per 64-key step the K and V code tiles (8 KB + 8 KB of e4m3 bytes for
+//     D = 128) are copied from global memory straight into LDS by buffer
+//     loads with the LDS-direct bit (16 bytes per lane, no VGPRs, no VALU);
+//     the XOR swizzle of the LDS rows is applied through the source
+//     addresses.  Two stages, issued one step ahead, one barrier per step.
 //   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 with the INT4 codes widened to
 //     fp8 e4m3 (exact for |code| <= 7; every partial sum is an integer below
 //     2^24, so the fp32 accumulator holds the exact integer score and no
@@ -41,10 +42,7 @@ struct Cfg {
   static constexpr int QC = D / 64;        // 64-channel chunks of the Q.K contraction
   static constexpr int DT = D / 32;        // 32-channel tiles of O
   static constexpr int KT = 64 * D;        // fp8 K tile: 64 rows of D bytes
-  static constexpr int VT = D * 64;        // int8 V tile: D rows of 64 slots
-  static constexpr int KPARTS = D / 32;    // 16-byte packed parts per key row
-  static constexpr int KP = 64 * KPARTS;   // packed K parts per tile
-  static constexpr int TOT = KP + 2 * D;   // + packed V parts (2 per channel)
+  static constexpr int VT = D * 64;        // fp8 V tile: D rows of 64 slots
 };
 
 // LDS rows are XOR-swizzled in 16-byte chunks.  The gfx950 LDS serves a
@@ -117,67 +115,55 @@ __device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt) {
   }
 }
 
-// Cooperative fetch of packed tiles into registers and widening store into
-// LDS.  The K part and the V part may belong to different key steps (the
-// pipelined main loop keeps K one step ahead of V); a negative index skips it.
-template <int D, int NT>
-struct TileLoad {
-  static constexpr int NP = (Cfg<D>::TOT + NT - 1) / NT;
-  static constexpr bool EXACT = Cfg<D>::TOT % NT == 0;
-  v4u r[NP];
+// ---- K/V staging: global memory -> LDS without registers ------------------
 
-  // Part p = threadIdx.x + i * NT.  KP and NT are multiples of 64, so whether
-  // a part is K or V is decided per wave; deriving it from the wave index
-  // (an SGPR) makes it a scalar branch rather than per-lane selects.
-  __device__ __forceinline__ static int wave_base(int i) {
-    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u)) + i * NT;
-  }
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+// Buffer load with the LDS-direct bit: lane i copies `size` bytes from
+// base(rsrc) + voffset into LDS at lds + size * i (lds is wave-uniform).
+extern "C" __device__ void ra_buffer_load_lds(v4i rsrc, lds_u32* lds, int size, int voffset, int soffset,
+                                              int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
-  __device__ __forceinline__ void fetch(const AttnArgs& a, int bh, int kt, int vt) {
-    using C = Cfg<D>;
+// Buffer descriptor over `bytes` bytes at `base` (reads past the end return 0).
+__device__ __forceinline__ v4i make_rsrc(const uint8_t* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+             __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)), (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Copies of one step's K tile (64 rows x D bytes) and V tile (D rows x 64
+// slot bytes) by NW waves.  The tiles are cut into 16-byte slots numbered in
+// LDS order; a wave copies 64 consecutive slots per instruction, K slots
+// first.  LDS slot (row r, physical chunk cp) holds logical chunk
+// cp ^ swizzle(r), so the source address carries the swizzle.
+template <int D, int NW>
+struct TileDma {
+  static constexpr int KS = Cfg<D>::KT / 16;
+  static constexpr int VS = Cfg<D>::VT / 16;
+  static constexpr int NI = (KS + VS) / (64 * NW);
+  static_assert(KS % 64 == 0 && (KS + VS) % (64 * NW) == 0, "slots must split evenly over waves");
+
+  // K tile kt -> kst, V tile vt -> vst; a negative index skips that tile.
+  __device__ __forceinline__ static void issue(const AttnArgs& a, int bh, int kt, int vt, uint8_t* kst,
+                                               uint8_t* vst) {
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int pb = wave_base(i);
-      const int p = pb + (threadIdx.x & 63);
-      const int pv = p - C::KP;
-      const bool isk = pb < C::KP;
-      const int t = isk ? kt : vt;
-      const uint8_t* src = isk
-          ? a.kp + ((size_t)bh * a.Npad + (size_t)kt * kBlock + p / C::KPARTS) * (D / 2) + (p % C::KPARTS) * 16
-          : a.vp + (((size_t)bh * a.nkb + vt) * D + (pv >> 1)) * 32 + (pv & 1) * 16;
-      if ((EXACT || pb < C::TOT) && t >= 0) r[i] = *reinterpret_cast<const v4u*>(src);
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* kst, uint8_t* vst, bool do_k, bool do_v) const {
-    using C = Cfg<D>;
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int pb = wave_base(i);
-      const int p = pb + (threadIdx.x & 63);
-      if (!EXACT && pb >= C::TOT) continue;
-      const int pv = p - C::KP;
-      const bool isk = pb < C::KP;
-      if (isk ? !do_k : !do_v) continue;
-      const int row = isk ? p / C::KPARTS : (pv >> 1);
-      const int c0 = 2 * (isk ? p % C::KPARTS : (pv & 1));
-      uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-      if (isk) {            // K codes -> fp8 e4m3 (QK runs on the fp8 MFMA)
-        unpack_e4m3(r[i][0], h0, l0);
-        unpack_e4m3(r[i][1], h1, l1);
-        unpack_e4m3(r[i][2], h2, l2);
-        unpack_e4m3(r[i][3], h3, l3);
-      } else {              // V codes -> fp8 e4m3 as well (PV runs on the fp8 MFMA)
-        unpack_e4m3(r[i][0], h0, l0);
-        unpack_e4m3(r[i][1], h1, l1);
-        unpack_e4m3(r[i][2], h2, l2);
-        unpack_e4m3(r[i][3], h3, l3);
+    for (int j = 0; j < NI; ++j) {
+      const int first = (j * NW + wave) * 64;            // wave-uniform
+      if (first < KS) {
+        if (kt < 0) continue;
+        const int s = first + lane, r = s / (D / 16), cp = s % (D / 16);
+        const int c = D == 128 ? cp ^ ((r >> 1) & 7) : cp ^ ((r >> 2) & 3);
+        const v4i rs = make_rsrc(a.kp + ((size_t)bh * a.Npad + (size_t)kt * kBlock) * D, Cfg<D>::KT);
+        ra_buffer_load_lds(rs, (lds_u32*)(kst + first * 16), 16, r * D + c * 16, 0, 0, 0);
+      } else {
+        if (vt < 0) continue;
+        const int s = first - KS + lane, r = s >> 2, cp = s & 3;
+        const int c = cp ^ ((r >> 2) & 3);
+        const v4i rs = make_rsrc(a.vp + ((size_t)bh * a.nkb + vt) * Cfg<D>::VT, Cfg<D>::VT);
+        ra_buffer_load_lds(rs, (lds_u32*)(vst + (first - KS) * 16), 16, r * 64 + c * 16, 0, 0, 0);
       }
-      uint8_t* base = isk ? kst : vst;
-      const int o0 = isk ? swz<D>(row, c0) : swz<64>(row, c0);
-      const int o1 = isk ? swz<D>(row, c0 + 1) : swz<64>(row, c0 + 1);
-      *reinterpret_cast<v4u*>(base + o0) = v4u{h0, h1, l0, l1};
-      *reinterpret_cast<v4u*>(base + o1) = v4u{h2, h3, l2, l3};
     }
   }
 };
@@ -189,15 +175,13 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int bh, int q, int hf,
                                        v8i (&qop)[Cfg<D>::QC]) {
 #pragma unroll
   for (int qc = 0; qc < Cfg<D>::QC; ++qc) {
-    v4u w = v4u{0u, 0u, 0u, 0u};
-    if (q < a.Npad)
-      w = *reinterpret_cast<const v4u*>(a.qp + ((size_t)bh * a.Npad + q) * (D / 2) + (qc * 4 + hf * 2) * 8);
-    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-    unpack_e4m3(w[0], h0, l0);
-    unpack_e4m3(w[1], h1, l1);
-    unpack_e4m3(w[2], h2, l2);
-    unpack_e4m3(w[3], h3, l3);
-    qop[qc] = v8i{(int)h0, (int)h1, (int)l0, (int)l1, (int)h2, (int)h3, (int)l2, (int)l3};
+    v4i w0 = v4i{0, 0, 0, 0}, w1 = w0;
+    if (q < a.Npad) {
+      const v4i* src = reinterpret_cast<const v4i*>(a.qp + ((size_t)bh * a.Npad + q) * D + qc * 64 + hf * 32);
+      w0 = src[0];
+      w1 = src[1];
+    }
+    qop[qc] = v8i{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
   }
 }
 
@@ -411,31 +395,28 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
 
   // Pipeline: during step t the wave computes S of step t+1 (K one stage
   // ahead) while it turns S of step t into P codes, then P x V of step t;
-  // one barrier per step.  At the end of step t, K of step t+2 and V of step
-  // t+1 are widened into the LDS stages freed by step t-1; their global
-  // loads were issued at the start of step t-1 into one of two register
-  // sets, so each load has a whole step to arrive.
-  TileLoad<D, 512> ldA, ldB;
-  ldA.fetch(a, bh, 0, -1);
-  ldA.store(kbuf, vbuf, true, false);
+  // one barrier per step.  At the start of step t the copies of K of step
+  // t+2 and V of step t+1 into the LDS stages freed by step t-1 are issued;
+  // they complete before the barrier that ends step t.
+  using Dma = TileDma<D, 8>;
+  Dma::issue(a, bh, 0, -1, kbuf, vbuf);
+  wait_lds_dma();
   __syncthreads();
-  ldA.fetch(a, bh, nkb > 1 ? 1 : -1, 0);
-  ldB.fetch(a, bh, nkb > 2 ? 2 : -1, nkb > 1 ? 1 : -1);
+  Dma::issue(a, bh, nkb > 1 ? 1 : -1, 0, kbuf + C::KT, vbuf);
   v16f s_cur[2];
   qk_step<D>(kbuf, qop, s_cur);
   const int nv0 = min(kBlock, a.N);
   if (nv0 < kBlock) mask_scores(s_cur, nv0);
   float cp_cur = score_scale(cq, sk[0], a.alpha_g);
   st.m = step_max(s_cur, cp_cur);
-  ldA.store(kbuf + C::KT, vbuf, nkb > 1, true);
+  wait_lds_dma();
   __syncthreads();
 
-  // One pipelined step; the score register sets and the staging register
-  // sets swap roles every step (the loop is unrolled by two so that no copy
-  // is needed).  lx holds K t+2 / V t+1, ly receives K t+3 / V t+2.
-  auto step = [&](v16f (&sc)[2], v16f (&sn)[2], TileLoad<D, 512>& lx, TileLoad<D, 512>& ly,
-                  int t) {
-    ly.fetch(a, bh, t + 3 < nkb ? t + 3 : -1, t + 2 < nkb ? t + 2 : -1);
+  // One pipelined step; the two score register sets swap roles every step
+  // (the loop is unrolled by two so that no copy is needed).
+  auto step = [&](v16f (&sc)[2], v16f (&sn)[2], int t) {
+    Dma::issue(a, bh, t + 2 < nkb ? t + 2 : -1, t + 1 < nkb ? t + 1 : -1, kbuf + (t & 1) * C::KT,
+               vbuf + ((t + 1) & 1) * C::VT);
     const uint8_t* kst = kbuf + ((t + 1) & 1) * C::KT;
     const uint8_t* vst = vbuf + (t & 1) * C::VT;
 
@@ -454,16 +435,16 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
       st.m = m_new;
       cp_cur = cp_next;
     }
-    lx.store(kbuf + (t & 1) * C::KT, vbuf + ((t + 1) & 1) * C::VT, t + 2 < nkb, t + 1 < nkb);
+    wait_lds_dma();
     __syncthreads();
   };
   v16f s_alt[2];
   int t = 0;
   for (; t + 1 < nkb; t += 2) {
-    step(s_cur, s_alt, ldB, ldA, t);
-    step(s_alt, s_cur, ldA, ldB, t + 1);
+    step(s_cur, s_alt, t);
+    step(s_alt, s_cur, t + 1);
   }
-  if (t < nkb) step(s_cur, s_alt, ldB, ldA, t);
+  if (t < nkb) step(s_cur, s_alt, t);
 
   // o = A s_v / L: the 1/15 of the dequantized P cancels against the
   // quantized row sum.
@@ -513,10 +494,9 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   const float cq = a.s_q[(size_t)bh * a.nblk + t.q_blk];
   State<D> st;
   state_init<D>(st);
-  TileLoad<D, 128> ld;
   for (int kb = 0; kb <= t.kv_blk; ++kb) {
-    ld.fetch(a, bh, kb, kb);
-    ld.store(smem, smem + C::KT, true, true);
+    TileDma<D, 2>::issue(a, bh, kb, kb, smem, smem + C::KT);
+    wait_lds_dma();
     __syncthreads();
     const int nvalid = min(kBlock, a.N - kb * kBlock);
     const float sk = a.s_k[(size_t)bh * a.nblk + kb];

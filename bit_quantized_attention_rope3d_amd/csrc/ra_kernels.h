@@ -10,7 +10,7 @@ namespace ra {
 struct QKPrologueArgs {
   const void* q;      // [B, N, H, D] bf16 or f32
   const void* k;
-  uint8_t* q_out;     // int4: [B*H, Npad, D/2] packed; bf16 path: [B*H, Npad, D] bf16
+  uint8_t* q_out;     // int4: [B*H, Npad, D] e4m3 code bytes; bf16 path: [B*H, Npad, D] bf16
   uint8_t* k_out;
   float* s_q;         // [B*H, nblk] (int4 path only)
   float* s_k;
@@ -27,13 +27,13 @@ struct VAmaxArgs {
 struct VQuantArgs {
   const void* v;
   const uint32_t* vamax;
-  uint8_t* v_out;     // int4: [B*H, nkb, D, 32] packed; bf16: [B*H, nkb, D, 64] bf16
+  uint8_t* v_out;     // int4: [B*H, nkb, D, 64] e4m3 code bytes; bf16: [B*H, nkb, D, 64] bf16
   float* s_v;         // [B*H, D]
   int N, H, nkb;
 };
 
 struct AttnArgs {
-  const uint8_t* qp;  // packed Q / K / V (int4) or bf16 tensors (bf16 path)
+  const uint8_t* qp;  // Q / K / V code bytes (int4) or bf16 tensors (bf16 path)
   const uint8_t* kp;
   const uint8_t* vp;
   const float* s_q;

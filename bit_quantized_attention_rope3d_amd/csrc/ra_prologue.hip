@@ -92,10 +92,6 @@ __device__ __forceinline__ int quant_code(float x, float inv) {
 }
 
 // Sign-magnitude nibble of a code in [-7, 7].
-__device__ __forceinline__ uint32_t sign_mag(int c) {
-  return c < 0 ? (8u | (uint32_t)(-c)) : (uint32_t)c;
-}
-
 __device__ __forceinline__ float block_max_256(float v, float* red) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -148,29 +144,22 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
   const float scale = amax / 7.0f;
   const float inv = 7.0f / amax;
 
-  uint32_t packed[PER / 8];
+  // One e4m3 byte per code, channel order: PER bytes per thread.
+  uint32_t packed[PER / 4];
 #pragma unroll
-  for (int g = 0; g < PER / 16; ++g) {
+  for (int w = 0; w < PER / 4; ++w) {
+    uint32_t acc = 0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        int i = half * 4 + bi;
-        int ch = amax > 0.0f ? quant_code(y[16 * g + i], inv) : 0;
-        int cl = amax > 0.0f ? quant_code(y[16 * g + i + 8], inv) : 0;
-        uint32_t byte = (sign_mag(ch) << 4) | sign_mag(cl);
-        w |= byte << (8 * bi);
-      }
-      packed[2 * g + half] = w;
+    for (int bi = 0; bi < 4; ++bi) {
+      const int c = amax > 0.0f ? quant_code(y[4 * w + bi], inv) : 0;
+      acc |= e4m3_of_code(c) << (8 * bi);
     }
+    packed[w] = acc;
   }
-  uint8_t* dst = out + ((size_t)bh * a.Npad + blk * kBlock + r) * (D / 2) + qq * (PER / 2);
-  if (PER / 2 == 16) {
-    *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  } else {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
-  }
+  uint4* dst = reinterpret_cast<uint4*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + qq * PER);
+#pragma unroll
+  for (int i = 0; i < PER / 16; ++i)
+    dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
   if (t == 0) sc[(size_t)bh * a.nblk + blk] = amax > 0.0f ? scale : 0.0f;
 }
 
@@ -214,7 +203,8 @@ __global__ void k_zero_u32(uint32_t* p, size_t n) {
 }
 
 // V quantization + transpose into the PV operand layout: one workgroup per
-// (64-key block, b*h); thread t owns channel 4t/4.. and two 16-slot groups.
+// (64-key block, b*h); each thread writes (channel, 16-slot group) units of
+// 16 e4m3 bytes.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
   constexpr int PER = D / 4;
@@ -241,22 +231,20 @@ __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
     const int d = unit >> 2, sg = unit & 3;
     const float amax = __uint_as_float(a.vamax[(size_t)bh * D + d]);
     const float inv = 7.0f / amax;
-    uint32_t w[2];
+    uint32_t w[4];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int q4 = 0; q4 < 4; ++q4) {
       uint32_t acc = 0;
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
-        int i = half * 4 + bi;
-        int kh = slot_key_pv(sg * 16 + i), kl = slot_key_pv(sg * 16 + i + 8);
-        int ch = amax > 0.0f ? quant_code(tile[kh][d], inv) : 0;
-        int cl = amax > 0.0f ? quant_code(tile[kl][d], inv) : 0;
-        acc |= ((sign_mag(ch) << 4) | sign_mag(cl)) << (8 * bi);
+        const int key = slot_key_pv(sg * 16 + 4 * q4 + bi);
+        const int c = amax > 0.0f ? quant_code(tile[key][d], inv) : 0;
+        acc |= e4m3_of_code(c) << (8 * bi);
       }
-      w[half] = acc;
+      w[q4] = acc;
     }
-    uint8_t* dst = a.v_out + (((size_t)bh * a.nkb + kb) * D + d) * 32 + sg * 8;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    uint8_t* dst = a.v_out + (((size_t)bh * a.nkb + kb) * D + d) * 64 + sg * 16;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     if (kb == 0 && sg == 0) a.s_v[(size_t)bh * D + d] = amax > 0.0f ? amax / 7.0f : 0.0f;
   }
 }

@@ -99,8 +99,9 @@ ra_status ra_plan_create(const ra_shape* shape, const ra_opts* opts, ra_plan* ou
 /* Release the plan and its device table copies.  Null is accepted. */
 ra_status ra_plan_destroy(ra_plan plan);
 
-/* Workspace bytes one ra_attn_fwd call of this plan needs (packed INT4
- * Q/K/V + scales, or the bf16 copies for the bf16 path). */
+/* Workspace bytes one ra_attn_fwd call of this plan needs (the INT4 codes
+ * of Q/K/V, one fp8 e4m3 byte each, + scales; or the bf16 copies for the
+ * bf16 path). */
 ra_status ra_plan_workspace_size(ra_plan plan, size_t* bytes);
 
 /* Same figure without a plan. */
