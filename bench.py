@@ -237,9 +237,10 @@ def main():
         del wsb, outb
         pb.close()
 
-    # Prologue: algorithmic bytes (bf16 Q, K, V read once; packed Q, K, V written).
+    # Prologue: algorithmic bytes (bf16 Q, K, V read once; one code byte per
+    # element of Q, K, V written).
     E = w.batch * w.tokens * w.heads * w.head_dim
-    pro_bytes = 3 * E * 2 + 3 * E // 2
+    pro_bytes = 3 * E * 2 + 3 * E
     traffic = traffic_for_current_kernel()
     roof = dict(bound="mfma", achieved=achieved_main, peak=INT8_PEAK_TOPS, unit="TFLOP/s",
                 frac=achieved_main / INT8_PEAK_TOPS, traffic=traffic,

@@ -388,7 +388,12 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
   v8i qop[C::QC];
   load_q<D>(a, bh, q0 + ln, hf, qop);
   const float cq = qblk < a.nblk ? a.s_q[(size_t)bh * a.nblk + qblk] : 0.0f;
-  const float* sk = a.s_k + (size_t)bh * a.nblk;
+  // K scales are read-only here and indexed by the (uniform) step: reading
+  // them through the constant address space makes them scalar loads, so
+  // waiting for one never waits on the vector-memory counter that tracks
+  // the K/V tile copies.
+  const __attribute__((address_space(4))) float* sk =
+      (const __attribute__((address_space(4))) float*)(a.s_k + (size_t)bh * a.nblk);
 
   State<D> st;
   state_init<D>(st);
