@@ -144,25 +144,39 @@ struct TileDma {
   static constexpr int NI = (KS + VS) / (64 * NW);
   static_assert(KS % 64 == 0 && (KS + VS) % (64 * NW) == 0, "slots must split evenly over waves");
 
-  // K tile kt -> kst, V tile vt -> vst; a negative index skips that tile.
-  __device__ __forceinline__ static void issue(const AttnArgs& a, int bh, int kt, int vt, uint8_t* kst,
-                                               uint8_t* vst) {
+  int off[NI];   // this lane's source byte offset within the tile, per instruction (step-invariant)
+
+  __device__ __forceinline__ TileDma() {
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int first = (j * NW + wave) * 64;
+      if (first < KS) {
+        const int s = first + lane, r = s / (D / 16), cp = s % (D / 16);
+        const int c = D == 128 ? cp ^ ((r >> 1) & 7) : cp ^ ((r >> 2) & 3);
+        off[j] = r * D + c * 16;
+      } else {
+        const int s = first - KS + lane, r = s >> 2, cp = s & 3;
+        off[j] = r * 64 + ((cp ^ ((r >> 2) & 3)) * 16);
+      }
+    }
+  }
+
+  // K tile kt -> kst, V tile vt -> vst; a negative index skips that tile.
+  __device__ __forceinline__ void issue(const AttnArgs& a, int bh, int kt, int vt, uint8_t* kst,
+                                        uint8_t* vst) const {
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int first = (j * NW + wave) * 64;            // wave-uniform
       if (first < KS) {
         if (kt < 0) continue;
-        const int s = first + lane, r = s / (D / 16), cp = s % (D / 16);
-        const int c = D == 128 ? cp ^ ((r >> 1) & 7) : cp ^ ((r >> 2) & 3);
         const v4i rs = make_rsrc(a.kp + ((size_t)bh * a.Npad + (size_t)kt * kBlock) * D, Cfg<D>::KT);
-        ra_buffer_load_lds(rs, (lds_u32*)(kst + first * 16), 16, r * D + c * 16, 0, 0, 0);
+        ra_buffer_load_lds(rs, (lds_u32*)(kst + first * 16), 16, off[j], 0, 0, 0);
       } else {
         if (vt < 0) continue;
-        const int s = first - KS + lane, r = s >> 2, cp = s & 3;
-        const int c = cp ^ ((r >> 2) & 3);
         const v4i rs = make_rsrc(a.vp + ((size_t)bh * a.nkb + vt) * Cfg<D>::VT, Cfg<D>::VT);
-        ra_buffer_load_lds(rs, (lds_u32*)(vst + (first - KS) * 16), 16, r * 64 + c * 16, 0, 0, 0);
+        ra_buffer_load_lds(rs, (lds_u32*)(vst + (first - KS) * 16), 16, off[j], 0, 0, 0);
       }
     }
   }
@@ -256,6 +270,25 @@ __device__ __forceinline__ void pmap_mtile(const v16f& s, float c, float m, cons
     const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x05010400u);   // e0 e1 u0 u1
     const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x05010400u);   // e2 e3 u2 u3
     p[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    U = __builtin_amdgcn_sad_u8(__builtin_amdgcn_perm(hi, lo, 0x07060302u), 0u, U);
+  }
+}
+
+// The P codes of a whole step (both M-tiles) with all 32 table loads in
+// flight at once: indices first, then the loads, then the packing, so the
+// LDS latency is paid once per step rather than once per group of codes.
+__device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c, float m, const uint8_t* tab,
+                                          uint32_t (&p)[2][4], uint32_t& U) {
+  uint32_t b[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) b[k] = ptab_index(s[k >> 4][k & 15], c, m);
+#pragma unroll
+  for (int k = 0; k < 32; ++k) b[k] = reinterpret_cast<const uint16_t*>(tab)[b[k]];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const uint32_t lo = __builtin_amdgcn_perm(b[4 * w + 1], b[4 * w], 0x05010400u);       // e0 e1 u0 u1
+    const uint32_t hi = __builtin_amdgcn_perm(b[4 * w + 3], b[4 * w + 2], 0x05010400u);   // e2 e3 u2 u3
+    p[w >> 2][w & 3] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     U = __builtin_amdgcn_sad_u8(__builtin_amdgcn_perm(hi, lo, 0x07060302u), 0u, U);
   }
 }
@@ -403,11 +436,11 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
   // one barrier per step.  At the start of step t the copies of K of step
   // t+2 and V of step t+1 into the LDS stages freed by step t-1 are issued;
   // they complete before the barrier that ends step t.
-  using Dma = TileDma<D, 8>;
-  Dma::issue(a, bh, 0, -1, kbuf, vbuf);
+  const TileDma<D, 8> dma;
+  dma.issue(a, bh, 0, -1, kbuf, vbuf);
   wait_lds_dma();
   __syncthreads();
-  Dma::issue(a, bh, nkb > 1 ? 1 : -1, 0, kbuf + C::KT, vbuf);
+  dma.issue(a, bh, nkb > 1 ? 1 : -1, 0, kbuf + C::KT, vbuf);
   v16f s_cur[2];
   qk_step<D>(kbuf, qop, s_cur);
   const int nv0 = min(kBlock, a.N);
@@ -420,15 +453,14 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
   // One pipelined step; the two score register sets swap roles every step
   // (the loop is unrolled by two so that no copy is needed).
   auto step = [&](v16f (&sc)[2], v16f (&sn)[2], int t) {
-    Dma::issue(a, bh, t + 2 < nkb ? t + 2 : -1, t + 1 < nkb ? t + 1 : -1, kbuf + (t & 1) * C::KT,
-               vbuf + ((t + 1) & 1) * C::VT);
+    dma.issue(a, bh, t + 2 < nkb ? t + 2 : -1, t + 1 < nkb ? t + 1 : -1, kbuf + (t & 1) * C::KT,
+              vbuf + ((t + 1) & 1) * C::VT);
     const uint8_t* kst = kbuf + ((t + 1) & 1) * C::KT;
     const uint8_t* vst = vbuf + (t & 1) * C::VT;
 
     qk_step<D>(kst, qop, sn);                     // S of step t+1 (unused after the last step)
     uint32_t p[2][4];
-    pmap_mtile(sc[0], cp_cur, st.m, ptab, p[0], st.U);
-    pmap_mtile(sc[1], cp_cur, st.m, ptab, p[1], st.U);
+    pmap_step(sc, cp_cur, st.m, ptab, p, st.U);
     pv_step<D>(vst, p, st.acc);
 
     if (t + 1 < nkb) {
@@ -499,8 +531,9 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   const float cq = a.s_q[(size_t)bh * a.nblk + t.q_blk];
   State<D> st;
   state_init<D>(st);
+  const TileDma<D, 2> dma;
   for (int kb = 0; kb <= t.kv_blk; ++kb) {
-    TileDma<D, 2>::issue(a, bh, kb, kb, smem, smem + C::KT);
+    dma.issue(a, bh, kb, kb, smem, smem + C::KT);
     wait_lds_dma();
     __syncthreads();
     const int nvalid = min(kBlock, a.N - kb * kBlock);
