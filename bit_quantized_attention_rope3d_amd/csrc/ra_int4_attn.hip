@@ -6,9 +6,11 @@
 // Sec. 4.2 (P mapped onto the full signed INT4 range: code = round(15 p) - 8).
 //
 // gfx950 design
-//   * One workgroup = 8 waves = 256 query rows of one (b, h); each wave owns 32
-//     queries.  Workgroup ids are remapped so that the workgroups resident on
-//     one XCD walk the same head, sharing K/V tiles in that XCD's L2.
+//   * One workgroup = 12 waves = 384 query rows of one (b, h); each wave owns
+//     32 queries.  A wave fits in 168 VGPRs, so three waves share each SIMD
+//     and hide one another's LDS and matrix-core latencies (one workgroup per
+//     CU).  Workgroup ids are remapped so that the workgroups resident on one
+//     XCD walk the same head, sharing K/V tiles in that XCD's L2.
 //   * Per 64-key step the K and V code tiles (8 KB + 8 KB of e4m3 bytes for
 //     D = 128) are copied from global memory straight into LDS by buffer
 //     loads with the LDS-direct bit (16 bytes per lane, no VGPRs, no VALU);
@@ -31,11 +33,14 @@
 //     are exact in e4m3 and a step's sums are integers below 2^24, so each
 //     step's PV is exact; it accumulates across steps in fp32 registers,
 //     scaled by beta only when a query's running max rises (rare after the
-//     first few steps).  A wave stays within 256 VGPRs (two waves per SIMD).
+//     first few steps).
 #include "ra_common.h"
 #include "ra_kernels.h"
 
 namespace ra {
+
+constexpr int kWaves = 12;                 // waves per workgroup
+constexpr int kQTile = 32 * kWaves;        // query rows per workgroup
 
 template <int D>
 struct Cfg {
@@ -141,8 +146,8 @@ template <int D, int NW>
 struct TileDma {
   static constexpr int KS = Cfg<D>::KT / 16;
   static constexpr int VS = Cfg<D>::VT / 16;
-  static constexpr int NI = (KS + VS) / (64 * NW);
-  static_assert(KS % 64 == 0 && (KS + VS) % (64 * NW) == 0, "slots must split evenly over waves");
+  static constexpr int NI = (KS + VS + 64 * NW - 1) / (64 * NW);
+  static_assert(KS % 64 == 0 && VS % 64 == 0, "tiles must be whole waves of slots");
 
   int off[NI];   // this lane's source byte offset within the tile, per instruction (step-invariant)
 
@@ -151,7 +156,9 @@ struct TileDma {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int first = (j * NW + wave) * 64;
-      if (first < KS) {
+      if (first >= KS + VS) {
+        off[j] = 0;
+      } else if (first < KS) {
         const int s = first + lane, r = s / (D / 16), cp = s % (D / 16);
         const int c = D == 128 ? cp ^ ((r >> 1) & 7) : cp ^ ((r >> 2) & 3);
         off[j] = r * D + c * 16;
@@ -169,6 +176,7 @@ struct TileDma {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int first = (j * NW + wave) * 64;            // wave-uniform
+      if (first >= KS + VS) continue;
       if (first < KS) {
         if (kt < 0) continue;
         const v4i rs = make_rsrc(a.kp + ((size_t)bh * a.Npad + (size_t)kt * kBlock) * D, Cfg<D>::KT);
@@ -398,23 +406,24 @@ __device__ __forceinline__ void state_init(State<D>& st) {
 }
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::KT + 2 * C::VT + kPTabBytes];
   uint8_t* const kbuf = smem;                     // 2 K stages
   uint8_t* const vbuf = smem + 2 * C::KT;         // 2 V stages
   uint8_t* const ptab = smem + 2 * C::KT + 2 * C::VT;
-  ptab_build(ptab, threadIdx.x, 512);             // visible after the first barrier
+  ptab_build(ptab, threadIdx.x, 64 * kWaves);     // visible after the first barrier
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of (head, query-tile) ids.
   const int nwg = gridDim.x, wg = blockIdx.x;
   const int full = nwg & ~7;
   const int lid = wg < full ? (wg & 7) * (full >> 3) + (wg >> 3) : wg;
-  const int bh = lid / a.nqt, qt = lid % a.nqt;
+  const int nqt = (a.N + kQTile - 1) / kQTile;
+  const int bh = lid / nqt, qt = lid % nqt;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
-  const int q0 = qt * 256 + wave * 32;
+  const int q0 = qt * kQTile + wave * 32;
   const int qblk = q0 >> 6;
   const int nkb = a.nkb;
 
@@ -431,57 +440,46 @@ __global__ __launch_bounds__(512) void k_int4_attn(AttnArgs a) {
   State<D> st;
   state_init<D>(st);
 
-  // Pipeline: during step t the wave computes S of step t+1 (K one stage
-  // ahead) while it turns S of step t into P codes, then P x V of step t;
-  // one barrier per step.  At the start of step t the copies of K of step
-  // t+2 and V of step t+1 into the LDS stages freed by step t-1 are issued;
-  // they complete before the barrier that ends step t.
-  const TileDma<D, 8> dma;
+  // Step t: P codes of step t (S in registers), S of step t+1, P x V of step
+  // t, then the running max of step t+1 and the rescale it may need; one
+  // barrier per step.  Within a wave these run in order; the other two
+  // waves on the SIMD fill the latencies.  At the start of step t the copies
+  // of K of step t+2 and V of step t+1 into the LDS stages freed by step t-1
+  // are issued; they complete before the barrier that ends step t.
+  const TileDma<D, kWaves> dma;
   dma.issue(a, bh, 0, -1, kbuf, vbuf);
   wait_lds_dma();
   __syncthreads();
   dma.issue(a, bh, nkb > 1 ? 1 : -1, 0, kbuf + C::KT, vbuf);
-  v16f s_cur[2];
-  qk_step<D>(kbuf, qop, s_cur);
-  const int nv0 = min(kBlock, a.N);
-  if (nv0 < kBlock) mask_scores(s_cur, nv0);
+  v16f s[2];
+  qk_step<D>(kbuf, qop, s);
+  {
+    const int nv0 = min(kBlock, a.N);
+    if (nv0 < kBlock) mask_scores(s, nv0);
+  }
   float cp_cur = score_scale(cq, sk[0], a.alpha_g);
-  st.m = step_max(s_cur, cp_cur);
+  st.m = step_max(s, cp_cur);
   wait_lds_dma();
   __syncthreads();
-
-  // One pipelined step; the two score register sets swap roles every step
-  // (the loop is unrolled by two so that no copy is needed).
-  auto step = [&](v16f (&sc)[2], v16f (&sn)[2], int t) {
+  for (int t = 0; t < nkb; ++t) {
     dma.issue(a, bh, t + 2 < nkb ? t + 2 : -1, t + 1 < nkb ? t + 1 : -1, kbuf + (t & 1) * C::KT,
               vbuf + ((t + 1) & 1) * C::VT);
-    const uint8_t* kst = kbuf + ((t + 1) & 1) * C::KT;
-    const uint8_t* vst = vbuf + (t & 1) * C::VT;
-
-    qk_step<D>(kst, qop, sn);                     // S of step t+1 (unused after the last step)
     uint32_t p[2][4];
-    pmap_step(sc, cp_cur, st.m, ptab, p, st.U);
-    pv_step<D>(vst, p, st.acc);
-
+    pmap_step(s, cp_cur, st.m, ptab, p, st.U);
+    qk_step<D>(kbuf + ((t + 1) & 1) * C::KT, qop, s);       // S of step t+1 (stale past the end)
+    pv_step<D>(vbuf + (t & 1) * C::VT, p, st.acc);
     if (t + 1 < nkb) {
       const int nv1 = min(kBlock, a.N - (t + 1) * kBlock);
-      if (nv1 < kBlock) mask_scores(sn, opaque_sgpr(nv1));
+      if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
       const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
-      const float m_new = fmaxf(st.m, step_max(sn, cp_next));
+      const float m_new = fmaxf(st.m, step_max(s, cp_next));
       if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
       st.m = m_new;
       cp_cur = cp_next;
     }
     wait_lds_dma();
     __syncthreads();
-  };
-  v16f s_alt[2];
-  int t = 0;
-  for (; t + 1 < nkb; t += 2) {
-    step(s_cur, s_alt, t);
-    step(s_alt, s_cur, t + 1);
   }
-  if (t < nkb) step(s_cur, s_alt, t);
 
   // o = A s_v / L: the 1/15 of the dequantized P cancels against the
   // quantized row sum.
@@ -570,13 +568,13 @@ __global__ void k_copy1(const uint8_t* __restrict__ src, uint8_t* __restrict__ d
 }
 
 void launch_int4_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st) {
-  const unsigned nwg = (unsigned)(B * a.H * a.nqt);
+  const unsigned nwg = (unsigned)(B * a.H * ((a.N + kQTile - 1) / kQTile));
   if (D == 128) {
-    if (out_bf16) k_int4_attn<128, true><<<nwg, 512, 0, st>>>(a);
-    else k_int4_attn<128, false><<<nwg, 512, 0, st>>>(a);
+    if (out_bf16) k_int4_attn<128, true><<<nwg, 64 * kWaves, 0, st>>>(a);
+    else k_int4_attn<128, false><<<nwg, 64 * kWaves, 0, st>>>(a);
   } else {
-    if (out_bf16) k_int4_attn<64, true><<<nwg, 512, 0, st>>>(a);
-    else k_int4_attn<64, false><<<nwg, 512, 0, st>>>(a);
+    if (out_bf16) k_int4_attn<64, true><<<nwg, 64 * kWaves, 0, st>>>(a);
+    else k_int4_attn<64, false><<<nwg, 64 * kWaves, 0, st>>>(a);
   }
 }
 
