@@ -45,44 +45,83 @@ __device__ __forceinline__ void load_row_part(const void* base, size_t elem_off,
   }
 }
 
-// RoPE pair rotation of channel i (segment-relative) of the row at LDS `row`:
-// (a, b) -> (a c - b s, a s + b c), each product rounded before the sum.
-__device__ __forceinline__ float rope_at(const float* row, int o, int i, const float* cs, const float* sn) {
-  int j = i >> 1;
-  float a = row[o + 2 * j], b = row[o + 2 * j + 1];
-  float c = cs[j], s = sn[j];
-  if ((i & 1) == 0) {
-    float ac = a * c;
-    float bs = b * s;
-    return ac - bs;
-  }
-  float as = a * s;
-  float bc = b * c;
-  return as + bc;
-}
+// Lane layout of the Q/K prologue kernels: a wave takes one token row at a
+// time (two rows when D = 64, lanes 0-31 and 32-63) and lane j holds RoPE
+// pair j, channels (2j, 2j+1), which lies in one segment (segment offsets
+// are even).  Loads of the row and of the segment tables are contiguous
+// across the lanes of a segment.
+template <int D>
+struct PairLane {
+  static constexpr int PAIRS = D / 2;
+  static constexpr int RPI = 64 / PAIRS;   // rows per wave step
+  int sub, j, s, jj, npair, off;           // row in the step, pair, segment, pair in segment, pairs in segment, channel offset
+  const float* cs;
+  const float* sn;
 
-// Rotated channel d: RoPE, then (ROT == 2) the Half rotation
-// u' = (u + w) r, w' = (u - w) r on (i, i + L/2), r = f32(1/sqrt 2).
-// ROT == 1 (Interleaved) is already merged into the tables as +pi/4.
-template <int ROT>
-__device__ __forceinline__ float rotated(const float* row, int d, const RopeTabs& t, const int* pos) {
-  int s = d < t.off[1] ? 0 : (d < t.off[2] ? 1 : 2);
-  int o = t.off[s], half = t.seg[s] >> 1;
-  int i = d - o;
-  const float* cs = t.cs[s] + (size_t)pos[s] * half;
-  const float* sn = t.sn[s] + (size_t)pos[s] * half;
-  if (ROT == 2) {
-    const float r = __uint_as_float(0x3F3504F3u);
-    if (i < half) {
-      float u = rope_at(row, o, i, cs, sn), w = rope_at(row, o, i + half, cs, sn);
-      float sum = u + w;
-      return sum * r;
-    }
-    float u = rope_at(row, o, i - half, cs, sn), w = rope_at(row, o, i, cs, sn);
-    float dif = u - w;
-    return dif * r;
+  __device__ __forceinline__ explicit PairLane(const RopeTabs& t) {
+    const int lane = threadIdx.x & 63;
+    sub = lane / PAIRS;
+    j = lane % PAIRS;
+    const int p1 = t.seg[0] >> 1, p2 = p1 + (t.seg[1] >> 1);
+    s = (j >= p1) + (j >= p2);
+    jj = j - (s == 0 ? 0 : (s == 1 ? p1 : p2));
+    npair = t.seg[s] >> 1;
+    off = t.off[s];
+    cs = t.cs[s];
+    sn = t.sn[s];
   }
-  return rope_at(row, o, i, cs, sn);
+
+  // RoPE of (x0, x1) at axis position pos of this lane's segment: each
+  // product rounded, then the difference / sum.
+  __device__ __forceinline__ void rope(int pos, float x0, float x1, float& y0, float& y1) const {
+    const float c = cs[pos * npair + jj], sv = sn[pos * npair + jj];
+    const float ac = x0 * c, bs = x1 * sv;
+    const float as = x0 * sv, bc = x1 * c;
+    y0 = ac - bs;
+    y1 = as + bc;
+  }
+};
+
+// Token n -> (frame, height, width) with w fastest, advanced row by row.
+struct GridPos {
+  int f, h, w;
+  __device__ __forceinline__ GridPos(int n, const RopeTabs& t) {
+    const int hw = t.dims[1] * t.dims[2];
+    f = n / hw;
+    h = (n - f * hw) / t.dims[2];
+    w = n - f * hw - h * t.dims[2];
+  }
+  // Advance by k <= 2 tokens: two conditional carries per axis suffice.
+  __device__ __forceinline__ void advance(int k, const RopeTabs& t) {
+    w += k;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool cw = w >= t.dims[2];
+      w = cw ? w - t.dims[2] : w;
+      h = cw ? h + 1 : h;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool ch = h >= t.dims[1];
+      h = ch ? h - t.dims[1] : h;
+      f = ch ? f + 1 : f;
+    }
+  }
+  __device__ __forceinline__ int axis(int s) const { return s == 0 ? f : (s == 1 ? h : w); }
+};
+
+// Two consecutive elements of a [B, N, H, D] row as fp32.
+template <bool BF16>
+__device__ __forceinline__ void load_pair(const void* base, size_t elem_off, float& x0, float& x1) {
+  if (BF16) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + elem_off);
+    x0 = __uint_as_float(w << 16);
+    x1 = __uint_as_float(w & 0xFFFF0000u);
+  } else {
+    const float2 v = *reinterpret_cast<const float2*>(static_cast<const float*>(base) + elem_off);
+    x0 = v.x;
+    x1 = v.y;
+  }
 }
 
 __device__ __forceinline__ int quant_code(float x, float inv) {
@@ -102,65 +141,75 @@ __device__ __forceinline__ float block_max_256(float v, float* red) {
 }
 
 // ---------------------------------------------------------------------------
-// Q/K: one workgroup per (64-token block, b*h, tensor).  256 threads: thread
-// t owns row t/4 and channels (t%4)*D/4 .. +D/4.
+// Q/K: one workgroup per (64-token block, b*h, tensor); each of the 4 waves
+// takes 16 rows of the block (PairLane layout).  RoPE per pair, then (ROT ==
+// 2) the Half rotation u' = (u + w) r, w' = (u - w) r on channels
+// (i, i + L/2) of each segment through a per-wave LDS row, r = f32(1/sqrt 2);
+// ROT == 1 (Interleaved) is already merged into the tables as +pi/4.  The
+// rotated values stay in registers for the block amax, then become e4m3
+// code bytes (2 per lane and row).
 template <int ROT, bool BF16, int D>
 __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
-  constexpr int PER = D / 4;
-  __shared__ float tile[64][D + 4];
+  using PL = PairLane<D>;
+  constexpr int ITERS = 16 / PL::RPI;
+  __shared__ float xch[4][PL::RPI][D];
   __shared__ float red[4];
   const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
   const int b = bh / a.H, h = bh % a.H;
   const void* x = which ? a.k : a.q;
   uint8_t* out = which ? a.k_out : a.q_out;
   float* sc = which ? a.s_k : a.s_q;
+  const int wave = threadIdx.x >> 6;
+  const PL pl(a.tabs);
+  const int r0 = wave * 16 + pl.sub;
+  GridPos gp(blk * kBlock + r0, a.tabs);
+  float* row = xch[wave][pl.sub];
 
-  const int t = threadIdx.x, r = t >> 2, qq = t & 3;
-  const int n = blk * kBlock + r;
-  if (n < a.N) {
-    load_row_part<BF16>(x, (((size_t)b * a.N + n) * a.H + h) * D + qq * PER, PER, &tile[r][qq * PER]);
-  } else {
-    for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = 0.0f;
-  }
-  __syncthreads();
-
-  float y[PER];
+  float y[ITERS][2];
   float mx = 0.0f;
-  if (n < a.N) {
-    int pos[3];
-    pos[0] = n / (a.tabs.dims[1] * a.tabs.dims[2]);
-    pos[1] = (n / a.tabs.dims[2]) % a.tabs.dims[1];
-    pos[2] = n % a.tabs.dims[2];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      y[e] = rotated<ROT>(tile[r], qq * PER + e, a.tabs, pos);
-      mx = fmaxf(mx, fabsf(y[e]));
+  for (int it = 0; it < ITERS; ++it) {
+    const int n = blk * kBlock + r0 + it * PL::RPI;
+    float x0 = 0.0f, x1 = 0.0f;
+    if (n < a.N) load_pair<BF16>(x, (((size_t)b * a.N + n) * a.H + h) * D + 2 * pl.j, x0, x1);
+    float v0, v1;
+    pl.rope(n < a.N ? gp.axis(pl.s) : 0, x0, x1, v0, v1);
+    if (ROT == 2) {
+      row[2 * pl.j] = v0;
+      row[2 * pl.j + 1] = v1;
+      __builtin_amdgcn_wave_barrier();
+      const float r = __uint_as_float(0x3F3504F3u);
+      const int hc = (2 * pl.npair) >> 1;      // L / 2 channels
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * pl.jj + e;
+        const float own = e ? v1 : v0;
+        const bool first = i < hc;                         // own is u, partner is w
+        const float other = row[pl.off + (first ? i + hc : i - hc)];
+        const float sum = own + other;
+        const float dif = other - own;
+        y[it][e] = (first ? sum : dif) * r;
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      y[it][0] = v0;
+      y[it][1] = v1;
     }
-  } else {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) y[e] = 0.0f;
+    mx = fmaxf(mx, fmaxf(fabsf(y[it][0]), fabsf(y[it][1])));
+    gp.advance(PL::RPI, a.tabs);
   }
   const float amax = block_max_256(mx, red);
   const float scale = amax / 7.0f;
   const float inv = 7.0f / amax;
-
-  // One e4m3 byte per code, channel order: PER bytes per thread.
-  uint32_t packed[PER / 4];
 #pragma unroll
-  for (int w = 0; w < PER / 4; ++w) {
-    uint32_t acc = 0;
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      const int c = amax > 0.0f ? quant_code(y[4 * w + bi], inv) : 0;
-      acc |= e4m3_of_code(c) << (8 * bi);
-    }
-    packed[w] = acc;
+  for (int it = 0; it < ITERS; ++it) {
+    const int r = r0 + it * PL::RPI;
+    const int c0 = amax > 0.0f ? quant_code(y[it][0], inv) : 0;
+    const int c1 = amax > 0.0f ? quant_code(y[it][1], inv) : 0;
+    *reinterpret_cast<uint16_t*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + 2 * pl.j) =
+        (uint16_t)(e4m3_of_code(c0) | (e4m3_of_code(c1) << 8));
   }
-  uint4* dst = reinterpret_cast<uint4*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + qq * PER);
-#pragma unroll
-  for (int i = 0; i < PER / 16; ++i)
-    dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
-  if (t == 0) sc[(size_t)bh * a.nblk + blk] = amax > 0.0f ? scale : 0.0f;
+  if (threadIdx.x == 0) sc[(size_t)bh * a.nblk + blk] = amax > 0.0f ? scale : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -254,37 +303,28 @@ __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
 // rounded to bf16, rows [b*h][Npad][D]; padded rows are zero.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void k_rope_bf16(QKPrologueArgs a) {
-  constexpr int PER = D / 4;
-  __shared__ float tile[64][D + 4];
+  using PL = PairLane<D>;
+  constexpr int ITERS = 16 / PL::RPI;
   const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
   const int b = bh / a.H, h = bh % a.H;
   const void* x = which ? a.k : a.q;
   uint16_t* out = reinterpret_cast<uint16_t*>(which ? a.k_out : a.q_out);
-  const int t = threadIdx.x, r = t >> 2, qq = t & 3;
-  const int n = blk * kBlock + r;
-  if (n < a.N) {
-    load_row_part<BF16>(x, (((size_t)b * a.N + n) * a.H + h) * D + qq * PER, PER, &tile[r][qq * PER]);
-  } else {
-    for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = 0.0f;
-  }
-  __syncthreads();
-  uint32_t packed[PER / 2];
-  int pos[3] = {0, 0, 0};
-  if (n < a.N) {
-    pos[0] = n / (a.tabs.dims[1] * a.tabs.dims[2]);
-    pos[1] = (n / a.tabs.dims[2]) % a.tabs.dims[1];
-    pos[2] = n % a.tabs.dims[2];
-  }
+  const int wave = threadIdx.x >> 6;
+  const PL pl(a.tabs);
+  const int r0 = wave * 16 + pl.sub;
+  GridPos gp(blk * kBlock + r0, a.tabs);
 #pragma unroll
-  for (int e = 0; e < PER; e += 2) {
-    float y0 = n < a.N ? rotated<0>(tile[r], qq * PER + e, a.tabs, pos) : 0.0f;
-    float y1 = n < a.N ? rotated<0>(tile[r], qq * PER + e + 1, a.tabs, pos) : 0.0f;
-    packed[e / 2] = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
+  for (int it = 0; it < ITERS; ++it) {
+    const int r = r0 + it * PL::RPI;
+    const int n = blk * kBlock + r;
+    float x0 = 0.0f, x1 = 0.0f;
+    if (n < a.N) load_pair<BF16>(x, (((size_t)b * a.N + n) * a.H + h) * D + 2 * pl.j, x0, x1);
+    float v0, v1;
+    pl.rope(n < a.N ? gp.axis(pl.s) : 0, x0, x1, v0, v1);
+    *reinterpret_cast<uint32_t*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + 2 * pl.j) =
+        (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+    gp.advance(PL::RPI, a.tabs);
   }
-  uint4* dst = reinterpret_cast<uint4*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + qq * PER);
-#pragma unroll
-  for (int i = 0; i < PER / 8; ++i)
-    dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
 }
 
 // V for the bf16 path: per 64-key block, [d][64 slots] bf16 in the bf16 PV
