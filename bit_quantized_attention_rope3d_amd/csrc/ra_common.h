@@ -7,6 +7,7 @@
 
 namespace ra {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -30,18 +31,30 @@ constexpr float kInvPGrid = 1.0f / 4755.0f;
 constexpr float kLog2Of15 = (float)3.9068905956085187;
 
 // Code layout in the workspace, shared by the prologue (writer) and the
-// attention kernels (readers).  Every INT4 code (Q, K, V in [-7, 7]) is
-// stored as one byte holding its fp8 e4m3 encoding, which is exact: gfx950
-// has no INT4 matrix instruction, so the codes are widened to the 8-bit
-// MFMA operand format once here, not in each query tile of the attention.
-//   * Q/K rows: D bytes per token in channel order.
-//   * V tile of one 64-key block: for each channel d, 64 bytes holding the
-//     64 key slots in MFMA operand order.
+// attention kernels (readers).  gfx950 has no INT4 matrix instruction, so
+// every INT4 code (Q, K, V in [-7, 7]) is stored already in the operand
+// format of the f8f6f4 MFMA that consumes it, chosen once here rather than
+// converted in each query tile of the attention.  Both encodings are exact
+// for integers in [-7, 7].
+//   * Q/K: fp6 e2m3 (6 bits per code), in tiles of 64 tokens (one scale
+//     block).  A tile holds D/32 channel groups; the 32 codes of (token r,
+//     group g) form 192 bits, code i at bits [6i, 6i+6), which is the
+//     operand one lane supplies for a 64-deep contraction chunk.  Bits
+//     0..127 of (r, g) are the 16 bytes at (64 g + r) * 16, bits 128..191
+//     the 8 bytes at (D/32) * 1024 + (64 g + r) * 8: one 64-token tile is
+//     48 * D bytes, read with one 16-byte and one 8-byte access per lane,
+//     consecutive tokens at consecutive addresses.
+//   * V tile of one 64-key block: fp8 e4m3 bytes; for each channel d, 64
+//     bytes holding the 64 key slots in MFMA operand order.
 //   Slot s = 32*hf + 16*mt + j (j < 16) carries key 32*mt + 8*(j/4) + 4*hf +
 //   (j%4): the key that the 32x32 accumulator of M-tile mt of S^T = K Q^T
 //   leaves in register j of lane half hf.  Lane half hf supplies K-elements
 //   32*hf..32*hf+31 of the PV MFMA's B operand, so the P codes of a lane are
 //   that operand as they stand, with no shuffle.
+__host__ __device__ constexpr int qk6_tile_bytes(int D) { return 48 * D; }
+__host__ __device__ constexpr int qk6_lo_off(int r, int g) { return (64 * g + r) * 16; }
+__host__ __device__ constexpr int qk6_hi_off(int D, int r, int g) { return (D / 32) * 1024 + (64 * g + r) * 8; }
+
 __host__ __device__ constexpr int slot_key_pv(int slot) {
   return 32 * ((slot >> 4) & 1) + 8 * ((slot & 15) >> 2) + 4 * (slot >> 5) + (slot & 3);
 }
@@ -57,6 +70,12 @@ __host__ __device__ constexpr int slot_key_bf16(int slot) {
 // |c| = 0..7 -> 00 38 40 44 48 4A 4C 4E.
 __host__ __device__ constexpr uint32_t e4m3_of_code(int c) {
   return (c < 0 ? 0x80u : 0u) | (uint32_t)((0x4E4C4A4844403800ull >> (8 * (c < 0 ? -c : c))) & 0xFFu);
+}
+
+// OCP fp6 e2m3 code (bits 0..5) of an integer c in [-7, 7] (exact): sign in
+// bit 5, |c| = 0..7 -> 00 08 10 14 18 1A 1C 1E.
+__host__ __device__ constexpr uint32_t e2m3_of_code(int c) {
+  return (c < 0 ? 0x20u : 0u) | (uint32_t)((0x1E1C1A1814100800ull >> (8 * (c < 0 ? -c : c))) & 0xFFu);
 }
 
 // Range-optimized P code, as u = code + 8 in [0, 15], of the grid exponent

@@ -104,10 +104,11 @@ Layout layout_of(const ra_shape* s, const ra_opts* o) {
   const size_t A = 256;
   size_t off = 0;
   if (o->prec == RA_PREC_INT4) {
-    const size_t tens = BH * L.Npad * D;     // one e4m3 byte per code
-    L.off_q = off; off = align_up(off + tens, A);
-    L.off_k = off; off = align_up(off + tens, A);
-    L.off_v = off; off = align_up(off + tens, A);
+    const size_t qk = BH * L.nblk * (size_t)ra::qk6_tile_bytes((int)D);   // fp6 tiles
+    const size_t vb = BH * L.Npad * D;                                     // one e4m3 byte per code
+    L.off_q = off; off = align_up(off + qk, A);
+    L.off_k = off; off = align_up(off + qk, A);
+    L.off_v = off; off = align_up(off + vb, A);
     L.off_sq = off; off = align_up(off + BH * L.nblk * 4, A);
     L.off_sk = off; off = align_up(off + BH * L.nblk * 4, A);
     L.off_sv = off; off = align_up(off + BH * D * 4, A);
@@ -459,31 +460,45 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
   const Layout& L = p->lay;
   const size_t BH = (size_t)p->shape.batch * p->shape.heads;
   const int D = p->shape.head_dim, N = L.N;
-  const size_t tens = BH * L.Npad * D;
-  std::vector<uint8_t> pq(tens), pk(tens), pv(tens);
+  const size_t qkb = BH * L.nblk * (size_t)ra::qk6_tile_bytes(D), tens = BH * L.Npad * D;
+  std::vector<uint8_t> pq(qkb), pk(qkb), pv(tens);
   const uint8_t* w = static_cast<const uint8_t*>(ws);
-  if (hipMemcpy(pq.data(), w + L.off_q, tens, hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemcpy(pk.data(), w + L.off_k, tens, hipMemcpyDeviceToHost) != hipSuccess ||
+  if (hipMemcpy(pq.data(), w + L.off_q, qkb, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(pk.data(), w + L.off_k, qkb, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(pv.data(), w + L.off_v, tens, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(s_q, w + L.off_sq, BH * L.nblk * 4, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(s_k, w + L.off_sk, BH * L.nblk * 4, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(s_v, w + L.off_sv, BH * D * 4, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(RA_ERR_HIP, "copy of prologue outputs failed");
-  // e4m3 byte -> code; bytes that encode no code in [-7, 7] decode to -128,
-  // which no valid code equals.
-  int8_t code_of[256];
+  // Encoded code -> integer code; encodings of no code in [-7, 7] decode to
+  // -128, which no valid code equals.
+  int8_t code_of[256], code_of6[64];
   for (int i = 0; i < 256; ++i) code_of[i] = INT8_MIN;
-  for (int c = -7; c <= 7; ++c) code_of[ra::e4m3_of_code(c)] = (int8_t)c;
+  for (int i = 0; i < 64; ++i) code_of6[i] = INT8_MIN;
+  for (int c = -7; c <= 7; ++c) {
+    code_of[ra::e4m3_of_code(c)] = (int8_t)c;
+    code_of6[ra::e2m3_of_code(c)] = (int8_t)c;
+  }
+  // Q/K: fp6 tiles of 64 tokens; (token r, group g) is 192 bits, code i at
+  // bits [6i, 6i+6): 16 bytes at the lo offset, then 8 at the hi offset.
+  const int tb = ra::qk6_tile_bytes(D);
   for (size_t bh = 0; bh < BH; ++bh)
     for (int n = 0; n < N; ++n) {
-      const uint8_t* rq = pq.data() + (bh * L.Npad + n) * D;
-      const uint8_t* rk = pk.data() + (bh * L.Npad + n) * D;
-      int8_t* oq = q_codes + (bh * N + n) * D;
-      int8_t* ok_ = k_codes + (bh * N + n) * D;
-      for (int d = 0; d < D; ++d) {
-        oq[d] = code_of[rq[d]];
-        ok_[d] = code_of[rk[d]];
-      }
+      const size_t tile = (bh * L.nblk + n / 64) * (size_t)tb;
+      const int r = n % 64;
+      for (int g = 0; g < D / 32; ++g)
+        for (int which = 0; which < 2; ++which) {
+          const uint8_t* t = (which ? pk.data() : pq.data()) + tile;
+          uint8_t bits[24];
+          std::memcpy(bits, t + ra::qk6_lo_off(r, g), 16);
+          std::memcpy(bits + 16, t + ra::qk6_hi_off(D, r, g), 8);
+          int8_t* o = (which ? k_codes : q_codes) + (bh * N + n) * D + 32 * g;
+          for (int i = 0; i < 32; ++i) {
+            const int b0 = 6 * i;
+            const unsigned v = (unsigned)bits[b0 / 8] | ((unsigned)(b0 / 8 + 1 < 24 ? bits[b0 / 8 + 1] : 0) << 8);
+            o[i] = code_of6[(v >> (b0 % 8)) & 0x3Fu];
+          }
+        }
     }
   // V: per 64-key block and channel, 64 slots in operand order.
   for (size_t bh = 0; bh < BH; ++bh)

@@ -11,16 +11,17 @@
 //     and hide one another's LDS and matrix-core latencies (one workgroup per
 //     CU).  Workgroup ids are remapped so that the workgroups resident on one
 //     XCD walk the same head, sharing K/V tiles in that XCD's L2.
-//   * Per 64-key step the K and V code tiles (8 KB + 8 KB of e4m3 bytes for
-//     D = 128) are copied from global memory straight into LDS by buffer
-//     loads with the LDS-direct bit (16 bytes per lane, no VGPRs, no VALU);
-//     the XOR swizzle of the LDS rows is applied through the source
-//     addresses.  Two stages, issued one step ahead, one barrier per step.
-//   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 with the INT4 codes widened to
-//     fp8 e4m3 (exact for |code| <= 7; every partial sum is an integer below
-//     2^24, so the fp32 accumulator holds the exact integer score and no
-//     int->float conversion is needed).  Each lane holds one query column, so
-//     row max / row sum are in-lane (+1 cross-half swap).
+//   * Per 64-key step the K and V code tiles (6 KB of fp6 + 8 KB of e4m3
+//     bytes for D = 128) are copied from global memory straight into LDS by
+//     buffer loads with the LDS-direct bit (16 bytes per lane, no VGPRs, no
+//     VALU); the XOR swizzle of the V rows is applied through the source
+//     addresses, the K tile needs none.  Two stages, issued one step ahead,
+//     one barrier per step.
+//   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 with both operands fp6 e2m3
+//     (exact for |code| <= 7, and twice the fp8 rate); every partial sum is
+//     an integer below 2^24, so the fp32 accumulator holds the exact integer
+//     score and no int->float conversion is needed.  Each lane holds one
+//     query column, so row max / row sum are in-lane (+1 cross-half swap).
 //   * P codes come straight out of the accumulator registers: the distance
 //     of each score below the running max, rounded to the exponent grid, is
 //     turned into an index with one FMA, one add and one saturating subtract
@@ -46,19 +47,16 @@ template <int D>
 struct Cfg {
   static constexpr int QC = D / 64;        // 64-channel chunks of the Q.K contraction
   static constexpr int DT = D / 32;        // 32-channel tiles of O
-  static constexpr int KT = 64 * D;        // fp8 K tile: 64 rows of D bytes
+  static constexpr int KT = qk6_tile_bytes(D);   // fp6 K tile of 64 keys (48 D bytes)
   static constexpr int VT = D * 64;        // fp8 V tile: D rows of 64 slots
 };
 
-// LDS rows are XOR-swizzled in 16-byte chunks.  The gfx950 LDS serves a
-// ds_read_b128 / ds_write_b128 in groups of 16 lanes over 64 banks (256 B);
-// the operand reads of one group touch 16 consecutive rows at one logical
-// chunk, so the swizzle must give those 16 rows 16 distinct 16-byte slots
-// of the 256-byte bank window: row parity (128-byte rows) or row mod 4
-// (64-byte rows) picks the half / quarter, the XOR picks the slot within it.
-template <int ROWBYTES>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  if (ROWBYTES == 128) return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+// V rows (64 bytes) are XOR-swizzled in 16-byte chunks in LDS.  The gfx950
+// LDS serves a ds_read_b128 in groups of 16 lanes over 64 banks (256 B); the
+// operand reads of one group touch 16 consecutive rows at one logical chunk,
+// so row mod 4 picks the quarter of the bank window and the XOR the slot
+// within it, giving the 16 rows 16 distinct 16-byte slots.
+__device__ __forceinline__ int swz64(int row, int chunk) {
   return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
@@ -70,28 +68,33 @@ struct State {
   uint32_t U;               // integer row sum of u since the last rescale (lane half)
 };
 
-// ---- range-optimized P map through an LDS byte table ----------------------
+// ---- range-optimized P map through an LDS table --------------------------
 //
 // For a score S with scale c and running max m (grid units), the grid
-// exponent is x = rint(f32(S c - m)) <= 0 and the code is u(x).  With
-// n = -x = rint(f32(m - S c)) (rounding is symmetric), the table holds
-// tab[i] = u(i - kPTabMax) for i <= kPTabMax and the index is
-// max(kPTabMax - n, 0): u vanishes for n >= kPTabMax.
-//   v = fma(S, -c, m)            f32(m - S c) >= 0, since m >= max S c
-//   w = v + 1.5 * 2^23           for v < 2^22: exactly 1.5*2^23 + rint(v)
-//                                (the add rounds to nearest even at unit
-//                                 spacing); larger, +inf and NaN land above
-//   i = sat(bits(1.5*2^23) + kPTabMax - bits(w))   unsigned saturating
-constexpr int kPTabMax = 23333;              // u(x) = 0 for x <= -kPTabMax
-constexpr int kPTabEntries = 23552;          // 16-bit entries (>= kPTabMax + 1)
+// exponent is x = rint(f32(S c - m)) <= 0 and the code is u(x); u(x) = 0 for
+// every x <= -2^15, so a table of u(-j), j = 0..2^15, covers all scores.
+// With c' = c 2^-15 and m' = m 2^-15 (exact power-of-two scalings):
+//   y = clamp(fma(S, -c', m'))   f32(m - S c) 2^-15 in [0, 1]: m >= max S c,
+//                                far keys saturate at 1, and with the DX10
+//                                clamp mode of compute kernels a NaN becomes
+//                                0, so y is in [0, 1] for every input
+//   w = y + 384                  the unit in the last place of 384 is 2^-15:
+//                                w = 384 + rint(f32(m - S c)) 2^-15 (round to
+//                                nearest even, as rint)
+//   a = 2 bits(w) - 2 bits(384)  byte offset of 16-bit entry j = -x, in
+//                                [0, 2^16] for every input
+constexpr int kPTabSpan = 1 << 15;
+constexpr int kPTabEntries = kPTabSpan + 2;                 // j = 0..2^15, padded to 4 bytes
 constexpr int kPTabBytes = 2 * kPTabEntries;
-constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
-constexpr uint32_t kPTabBase = 0x4B400000u + (uint32_t)kPTabMax;
+constexpr float kPTabScale = 1.0f / 32768.0f;               // 2^-15
+constexpr uint32_t kPTabBias = 0u - 2u * 0x43C00000u;       // -2 bits(384) mod 2^32
+constexpr uint32_t kPTabZero = 2u * kPTabSpan;              // entry of j = 2^15: u = 0
 
-__device__ __forceinline__ uint32_t ptab_index(float s, float c, float m) {
-  const float v = __builtin_fmaf(s, -c, m);
-  const float w = v + kRoundMagic;
-  return __builtin_elementwise_sub_sat(kPTabBase, __float_as_uint(w));
+__device__ __forceinline__ uint32_t ptab_addr(float s, float c2, float m2) {
+  float y;
+  asm("v_fma_f32 %0, %1, -%2, %3 clamp" : "=v"(y) : "v"(s), "v"(c2), "v"(m2));
+  const float w = y + 384.0f;
+  return (__float_as_uint(w) << 1) + kPTabBias;
 }
 
 // e4m3 encoding of an integer 0 <= u <= 15 (exact).
@@ -109,14 +112,12 @@ __device__ __forceinline__ uint32_t e4m3_to_uint(uint32_t b) {
 }
 
 // Fill the table cooperatively (threads tid, tid + nt, ...) from the exp2
-// form of the map, exact on every grid point: entry i = e4m3(u) | u << 8 for
-// u = u(i - kPTabMax).  Entries past kPTabMax are never indexed by a valid
-// running max; they hold u(0).
+// form of the map, exact on every grid point: entry j = e4m3(u) | u << 8 for
+// u = u(-j).
 __device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt) {
-  for (int i = tid; i < kPTabEntries; i += nt) {
-    const float x = (float)(min(i, kPTabMax) - kPTabMax);
-    const uint32_t u = pmap_insert(x, 0u, 0u) & 0xFFu;
-    reinterpret_cast<uint16_t*>(tab)[i] = (uint16_t)(e4m3_of_uint(u) | (u << 8));
+  for (int j = tid; j < kPTabEntries; j += nt) {
+    const uint32_t u = pmap_insert(-(float)j, 0u, 0u) & 0xFFu;
+    reinterpret_cast<uint16_t*>(tab)[j] = (uint16_t)(e4m3_of_uint(u) | (u << 8));
   }
 }
 
@@ -137,11 +138,12 @@ __device__ __forceinline__ v4i make_rsrc(const uint8_t* base, uint32_t bytes) {
 
 __device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Copies of one step's K tile (64 rows x D bytes) and V tile (D rows x 64
+// Copies of one step's K tile (fp6, 48 D bytes) and V tile (D rows x 64
 // slot bytes) by NW waves.  The tiles are cut into 16-byte slots numbered in
 // LDS order; a wave copies 64 consecutive slots per instruction, K slots
-// first.  LDS slot (row r, physical chunk cp) holds logical chunk
-// cp ^ swizzle(r), so the source address carries the swizzle.
+// first.  K slots are copied in place; V slot (row r, physical chunk cp)
+// holds logical chunk cp ^ swizzle(r), so the source address carries the
+// swizzle.
 template <int D, int NW>
 struct TileDma {
   static constexpr int KS = Cfg<D>::KT / 16;
@@ -149,7 +151,12 @@ struct TileDma {
   static constexpr int NI = (KS + VS + 64 * NW - 1) / (64 * NW);
   static_assert(KS % 64 == 0 && VS % 64 == 0, "tiles must be whole waves of slots");
 
-  int off[NI];   // this lane's source byte offset within the tile, per instruction (step-invariant)
+  // Per instruction j (all step-invariant): this lane's source byte offset
+  // within its tile, and, uniform over the wave, which tile the wave's 64
+  // slots belong to (0 none, 1 K, 2 V) and their byte offset in the stage.
+  int off[NI];
+  int kind[NI];
+  int lds[NI];
 
   __device__ __forceinline__ TileDma() {
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
@@ -157,53 +164,52 @@ struct TileDma {
     for (int j = 0; j < NI; ++j) {
       const int first = (j * NW + wave) * 64;
       if (first >= KS + VS) {
+        kind[j] = 0;
+        lds[j] = 0;
         off[j] = 0;
       } else if (first < KS) {
-        const int s = first + lane, r = s / (D / 16), cp = s % (D / 16);
-        const int c = D == 128 ? cp ^ ((r >> 1) & 7) : cp ^ ((r >> 2) & 3);
-        off[j] = r * D + c * 16;
+        kind[j] = 1;
+        lds[j] = first * 16;
+        off[j] = (first + lane) * 16;          // the fp6 K tile is copied as it lies
       } else {
         const int s = first - KS + lane, r = s >> 2, cp = s & 3;
+        kind[j] = 2;
+        lds[j] = (first - KS) * 16;
         off[j] = r * 64 + ((cp ^ ((r >> 2) & 3)) * 16);
       }
+      kind[j] = __builtin_amdgcn_readfirstlane(kind[j]);
+      lds[j] = __builtin_amdgcn_readfirstlane(lds[j]);
     }
   }
 
-  // K tile kt -> kst, V tile vt -> vst; a negative index skips that tile.
-  __device__ __forceinline__ void issue(const AttnArgs& a, int bh, int kt, int vt, uint8_t* kst,
-                                        uint8_t* vst) const {
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // K tile at kt -> kst, V tile at vt -> vst (global addresses of the
+  // tiles); a null tile is skipped.
+  __device__ __forceinline__ void issue(const uint8_t* kt, const uint8_t* vt, uint8_t* kst, uint8_t* vst) const {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int first = (j * NW + wave) * 64;            // wave-uniform
-      if (first >= KS + VS) continue;
-      if (first < KS) {
-        if (kt < 0) continue;
-        const v4i rs = make_rsrc(a.kp + ((size_t)bh * a.Npad + (size_t)kt * kBlock) * D, Cfg<D>::KT);
-        ra_buffer_load_lds(rs, (lds_u32*)(kst + first * 16), 16, off[j], 0, 0, 0);
-      } else {
-        if (vt < 0) continue;
-        const v4i rs = make_rsrc(a.vp + ((size_t)bh * a.nkb + vt) * Cfg<D>::VT, Cfg<D>::VT);
-        ra_buffer_load_lds(rs, (lds_u32*)(vst + (first - KS) * 16), 16, off[j], 0, 0, 0);
-      }
+      if (kind[j] == 1 && kt != nullptr)
+        ra_buffer_load_lds(make_rsrc(kt, Cfg<D>::KT), (lds_u32*)(kst + lds[j]), 16, off[j], 0, 0, 0);
+      else if (kind[j] == 2 && vt != nullptr)
+        ra_buffer_load_lds(make_rsrc(vt, Cfg<D>::VT), (lds_u32*)(vst + lds[j]), 16, off[j], 0, 0, 0);
     }
   }
 };
 
-// Q operands (B operand of S^T = K Q^T on the fp8 MFMA): query `q`,
-// channels 64qc + 32hf + 0..31 as e4m3 bytes.
+// Q operands (B operand of S^T = K Q^T on the f8f6f4 MFMA, fp6): query `q`,
+// channels 64qc + 32hf + 0..31, i.e. channel group 2qc + hf of its tile.
 template <int D>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int bh, int q, int hf,
                                        v8i (&qop)[Cfg<D>::QC]) {
 #pragma unroll
   for (int qc = 0; qc < Cfg<D>::QC; ++qc) {
-    v4i w0 = v4i{0, 0, 0, 0}, w1 = w0;
+    v4i lo = v4i{0, 0, 0, 0};
+    v2i hi = v2i{0, 0};
     if (q < a.Npad) {
-      const v4i* src = reinterpret_cast<const v4i*>(a.qp + ((size_t)bh * a.Npad + q) * D + qc * 64 + hf * 32);
-      w0 = src[0];
-      w1 = src[1];
+      const uint8_t* t = a.qp + ((size_t)bh * a.nblk + (q >> 6)) * Cfg<D>::KT;
+      lo = *reinterpret_cast<const v4i*>(t + qk6_lo_off(q & 63, 2 * qc + hf));
+      hi = *reinterpret_cast<const v2i*>(t + qk6_hi_off(D, q & 63, 2 * qc + hf));
     }
-    qop[qc] = v8i{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    qop[qc] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
   }
 }
 
@@ -214,7 +220,10 @@ __device__ __forceinline__ int acc_key(int mt, int r, int hf) {
 
 // ---- building blocks of one 64-key step for the 32 queries of a wave ------
 
-// S^T of the step (exact integers in fp32): kst is the step's fp8 K tile.
+// S^T of the step (exact integers in fp32): kst is the step's fp6 K tile.
+// Lane (ln, hf) supplies key row 32mt + ln, channel group 2qc + hf: one
+// 16-byte and one 8-byte LDS read, consecutive rows at consecutive
+// addresses (no bank conflicts without a swizzle).
 template <int D>
 __device__ __forceinline__ void qk_step(const uint8_t* kst, const v8i (&qop)[Cfg<D>::QC], v16f (&s)[2]) {
   const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
@@ -224,11 +233,11 @@ __device__ __forceinline__ void qk_step(const uint8_t* kst, const v8i (&qop)[Cfg
     for (int r = 0; r < 16; ++r) s[mt][r] = 0.0f;
 #pragma unroll
     for (int qc = 0; qc < Cfg<D>::QC; ++qc) {
-      const int row = mt * 32 + ln, c0 = qc * 4 + hf * 2;
-      const v4i k0 = *reinterpret_cast<const v4i*>(kst + swz<D>(row, c0));
-      const v4i k1 = *reinterpret_cast<const v4i*>(kst + swz<D>(row, c0 + 1));
-      const v8i ka = v8i{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-      s[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qop[qc], s[mt], 0, 0, 0, 0, 0, 0);
+      const int row = mt * 32 + ln, g = 2 * qc + hf;
+      const v4i lo = *reinterpret_cast<const v4i*>(kst + qk6_lo_off(row, g));
+      const v2i hi = *reinterpret_cast<const v2i*>(kst + qk6_hi_off(D, row, g));
+      const v8i ka = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+      s[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qop[qc], s[mt], 2, 2, 0, 0, 0, 0);
     }
   }
 }
@@ -264,41 +273,46 @@ __device__ __forceinline__ float step_max(const v16f (&s)[2], float c) {
   return mul_round_up(mx, c);
 }
 
-// P codes of M-tile mt (u = code + 8) as e4m3 bytes, half of the 32-byte B
-// operand of the PV MFMA: register 4i+e of the tile goes to byte e of word
-// i.  U accumulates the integer u (v_sad_u8 over the four high bytes).  Keys
-// masked to S = -inf give v = +inf (or NaN when c = 0) and thus u = 0.
-__device__ __forceinline__ void pmap_mtile(const v16f& s, float c, float m, const uint8_t* tab,
-                                           uint32_t (&p)[4], uint32_t& U) {
+// P codes of a whole step (u = code + 8 in e4m3, both M-tiles) in the order
+// of the PV MFMA's B operand: register 4i+e of M-tile mt goes to byte e of
+// p[mt][i].  U accumulates the integer u.  All 32 table loads are issued
+// before any is used, so the LDS latency is paid once per step; each pair of
+// 16-bit entries lands in the two halves of one register (e0 u0 e1 u1), and
+// one v_perm per four codes gathers the e4m3 bytes.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c2, float m2, const uint8_t* tab,
+                                          uint32_t (&p)[2][4], uint32_t& U) {
+  uint32_t a[32];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t b[4];
+  for (int k = 0; k < 32; ++k) a[k] = ptab_addr(s[k >> 4][k & 15], c2, m2);
+  uint32_t r[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) b[e] = reinterpret_cast<const uint16_t*>(tab)[ptab_index(s[4 * i + e], c, m)];
-    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x05010400u);   // e0 e1 u0 u1
-    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x05010400u);   // e2 e3 u2 u3
-    p[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    U = __builtin_amdgcn_sad_u8(__builtin_amdgcn_perm(hi, lo, 0x07060302u), 0u, U);
+  for (int i = 0; i < 16; ++i) {
+    const u16x2 v = u16x2{*reinterpret_cast<const uint16_t*>(tab + a[2 * i]),
+                          *reinterpret_cast<const uint16_t*>(tab + a[2 * i + 1])};
+    r[i] = __builtin_bit_cast(uint32_t, v);
+  }
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    p[w >> 2][w & 3] = __builtin_amdgcn_perm(r[2 * w + 1], r[2 * w], 0x06040200u);           // e0 e1 e2 e3
+    U = __builtin_amdgcn_sad_u8(__builtin_amdgcn_perm(r[2 * w + 1], r[2 * w], 0x07050301u), 0u, U);
   }
 }
 
-// The P codes of a whole step (both M-tiles) with all 32 table loads in
-// flight at once: indices first, then the loads, then the packing, so the
-// LDS latency is paid once per step rather than once per group of codes.
-__device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c, float m, const uint8_t* tab,
-                                          uint32_t (&p)[2][4], uint32_t& U) {
-  uint32_t b[32];
+// Padded keys of a ragged last step carry S = -inf.  With c > 0 they read
+// the last entry (u = 0); with c = 0 the product is NaN, which the clamp
+// turns into 0, so they read entry 0 (u = 15).  Their V codes are 0, so
+// only the row sum needs a correction: the u this lane's padded keys added.
+__device__ __forceinline__ uint32_t padded_u(float c2, int nvalid) {
+  if (c2 != 0.0f) return 0u;
+  const int hf = (threadIdx.x & 63) >> 5;
+  int nv = 0;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) b[k] = ptab_index(s[k >> 4][k & 15], c, m);
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-  for (int k = 0; k < 32; ++k) b[k] = reinterpret_cast<const uint16_t*>(tab)[b[k]];
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    const uint32_t lo = __builtin_amdgcn_perm(b[4 * w + 1], b[4 * w], 0x05010400u);       // e0 e1 u0 u1
-    const uint32_t hi = __builtin_amdgcn_perm(b[4 * w + 3], b[4 * w + 2], 0x05010400u);   // e2 e3 u2 u3
-    p[w >> 2][w & 3] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    U = __builtin_amdgcn_sad_u8(__builtin_amdgcn_perm(hi, lo, 0x07060302u), 0u, U);
-  }
+    for (int g = 0; g < 4; ++g) nv += min(max(nvalid - (32 * mt + 8 * g + 4 * hf), 0), 4);
+  return 15u * (uint32_t)(32 - nv);
 }
 
 // O^T += V^T P^T over the 64 keys of the step: lane half hf supplies slots
@@ -312,8 +326,8 @@ __device__ __forceinline__ void pv_step(const uint8_t* vst, const uint32_t (&p)[
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
     const int row = dt * 32 + ln;
-    const v4i v0 = *reinterpret_cast<const v4i*>(vst + swz<64>(row, 2 * hf));
-    const v4i v1 = *reinterpret_cast<const v4i*>(vst + swz<64>(row, 2 * hf + 1));
+    const v4i v0 = *reinterpret_cast<const v4i*>(vst + swz64(row, 2 * hf));
+    const v4i v1 = *reinterpret_cast<const v4i*>(vst + swz64(row, 2 * hf + 1));
     const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[dt], 0, 0, 0, 0, 0, 0);
   }
@@ -355,8 +369,8 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
   if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
   st.m = m_new;
   uint32_t p[2][4];
-  pmap_mtile(s[0], cp, m_new, tab, p[0], st.U);
-  pmap_mtile(s[1], cp, m_new, tab, p[1], st.U);
+  pmap_step(s, cp * kPTabScale, m_new * kPTabScale, tab, p, st.U);
+  if (nvalid < kBlock) st.U -= padded_u(cp * kPTabScale, nvalid);
   pv_step<D>(vst, p, st.acc);
 
   if (DUMP) {
@@ -373,7 +387,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
         if (r % 4 == 0) ones[mt][r >> 2] = 0u;
         if (key < nvalid) ones[mt][r >> 2] |= 0x38u << (8 * (r & 3));   // e4m3 1.0
         const int sv = key < nvalid ? (int)s[mt][r] : 0;
-        const int code = (int)e4m3_to_uint((p[mt][r >> 2] >> (8 * (r & 3))) & 0xFFu) - 8;
+        const int code = key < nvalid ? (int)e4m3_to_uint((p[mt][r >> 2] >> (8 * (r & 3))) & 0xFFu) - 8 : -8;
         dump->s_int[qrow * 64 + key] = sv;
         dump->p_code[qrow * 64 + key] = (int8_t)code;
       }
@@ -447,10 +461,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   // of K of step t+2 and V of step t+1 into the LDS stages freed by step t-1
   // are issued; they complete before the barrier that ends step t.
   const TileDma<D, kWaves> dma;
-  dma.issue(a, bh, 0, -1, kbuf, vbuf);
+  const uint8_t* const ktiles = a.kp + (size_t)bh * a.nblk * C::KT;
+  const uint8_t* const vtiles = a.vp + (size_t)bh * a.nkb * C::VT;
+  dma.issue(ktiles, nullptr, kbuf, vbuf);
   wait_lds_dma();
   __syncthreads();
-  dma.issue(a, bh, nkb > 1 ? 1 : -1, 0, kbuf + C::KT, vbuf);
+  dma.issue(nkb > 1 ? ktiles + C::KT : nullptr, vtiles, kbuf + C::KT, vbuf);
   v16f s[2];
   qk_step<D>(kbuf, qop, s);
   {
@@ -461,24 +477,33 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   st.m = step_max(s, cp_cur);
   wait_lds_dma();
   __syncthreads();
-  for (int t = 0; t < nkb; ++t) {
-    dma.issue(a, bh, t + 2 < nkb ? t + 2 : -1, t + 1 < nkb ? t + 1 : -1, kbuf + (t & 1) * C::KT,
-              vbuf + ((t + 1) & 1) * C::VT);
+  const uint8_t* kt2 = ktiles + 2 * C::KT;      // K tile of step t + 2
+  const uint8_t* vt1 = vtiles + C::VT;          // V tile of step t + 1
+#pragma nounroll
+  for (int t = 0; t + 1 < nkb; ++t, kt2 += C::KT, vt1 += C::VT) {
+    dma.issue(t + 2 < nkb ? kt2 : nullptr, vt1, kbuf + (t & 1) * C::KT, vbuf + ((t + 1) & 1) * C::VT);
     uint32_t p[2][4];
-    pmap_step(s, cp_cur, st.m, ptab, p, st.U);
-    qk_step<D>(kbuf + ((t + 1) & 1) * C::KT, qop, s);       // S of step t+1 (stale past the end)
+    pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale, ptab, p, st.U);
+    qk_step<D>(kbuf + ((t + 1) & 1) * C::KT, qop, s);       // S of step t+1
     pv_step<D>(vbuf + (t & 1) * C::VT, p, st.acc);
-    if (t + 1 < nkb) {
-      const int nv1 = min(kBlock, a.N - (t + 1) * kBlock);
-      if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
-      const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
-      const float m_new = fmaxf(st.m, step_max(s, cp_next));
-      if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
-      st.m = m_new;
-      cp_cur = cp_next;
-    }
+    const int nv1 = min(kBlock, a.N - (t + 1) * kBlock);
+    if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
+    const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
+    const float m_new = fmaxf(st.m, step_max(s, cp_next));
+    if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
+    st.m = m_new;
+    cp_cur = cp_next;
     wait_lds_dma();
     __syncthreads();
+  }
+  {
+    // The last step: its V tile was copied during the step before (or
+    // before the loop when nkb = 1).
+    const int t = nkb - 1, nvalid = a.N - t * kBlock;
+    uint32_t p[2][4];
+    pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale, ptab, p, st.U);
+    if (nvalid < kBlock) st.U -= padded_u(cp_cur * kPTabScale, nvalid);
+    pv_step<D>(vbuf + (t & 1) * C::VT, p, st.acc);
   }
 
   // o = A s_v / L: the 1/15 of the dequantized P cancels against the
@@ -531,7 +556,8 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   state_init<D>(st);
   const TileDma<D, 2> dma;
   for (int kb = 0; kb <= t.kv_blk; ++kb) {
-    dma.issue(a, bh, kb, kb, smem, smem + C::KT);
+    dma.issue(a.kp + ((size_t)bh * a.nblk + kb) * C::KT, a.vp + ((size_t)bh * a.nkb + kb) * C::VT, smem,
+              smem + C::KT);
     wait_lds_dma();
     __syncthreads();
     const int nvalid = min(kBlock, a.N - kb * kBlock);
@@ -553,7 +579,7 @@ __global__ __launch_bounds__(256) void k_pmap_probe(const float* __restrict__ x,
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
-    u[i] = (uint8_t)(reinterpret_cast<const uint16_t*>(tab)[ptab_index(x[i], 1.0f, 0.0f)] >> 8);
+    u[i] = (uint8_t)(*reinterpret_cast<const uint16_t*>(tab + ptab_addr(x[i], kPTabScale, 0.0f)) >> 8);
 }
 
 __global__ void k_copy16(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n16) {

@@ -10,7 +10,7 @@ namespace ra {
 struct QKPrologueArgs {
   const void* q;      // [B, N, H, D] bf16 or f32
   const void* k;
-  uint8_t* q_out;     // int4: [B*H, Npad, D] e4m3 code bytes; bf16 path: [B*H, Npad, D] bf16
+  uint8_t* q_out;     // int4: [B*H, nblk] 64-token fp6 e2m3 tiles (48 D bytes each); bf16 path: [B*H, Npad, D] bf16
   uint8_t* k_out;
   float* s_q;         // [B*H, nblk] (int4 path only)
   float* s_k;

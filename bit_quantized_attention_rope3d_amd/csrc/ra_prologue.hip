@@ -130,7 +130,7 @@ __device__ __forceinline__ int quant_code(float x, float inv) {
   return (int)q;
 }
 
-// Sign-magnitude nibble of a code in [-7, 7].
+// Maximum of v over the 256 threads of the workgroup (red: 4 floats of LDS).
 __device__ __forceinline__ float block_max_256(float v, float* red) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -140,20 +140,41 @@ __device__ __forceinline__ float block_max_256(float v, float* red) {
   return m;
 }
 
+// Bits [32 W, 32 W + 32) of the 192-bit fp6 string of one (token, channel
+// group): cw holds the group's 32 codes, one 6-bit code per byte.
+template <int W>
+__device__ __forceinline__ uint32_t fp6_word(const uint32_t (&cw)[8]) {
+  constexpr int c_lo = 32 * W / 6;
+  constexpr int c_hi = (32 * W + 31) / 6 < 31 ? (32 * W + 31) / 6 : 31;
+  uint64_t acc = 0;
+#pragma unroll
+  for (int c = c_lo; c <= c_hi; ++c)
+    acc |= (uint64_t)((cw[c >> 2] >> (8 * (c & 3))) & 0x3Fu) << (6 * (c - c_lo));
+  return (uint32_t)(acc >> (32 * W - 6 * c_lo));
+}
+
+__device__ __forceinline__ void load_group_codes(const uint8_t* p, uint32_t (&cw)[8]) {
+  const uint4 a = reinterpret_cast<const uint4*>(p)[0], b = reinterpret_cast<const uint4*>(p)[1];
+  cw[0] = a.x; cw[1] = a.y; cw[2] = a.z; cw[3] = a.w;
+  cw[4] = b.x; cw[5] = b.y; cw[6] = b.z; cw[7] = b.w;
+}
+
 // ---------------------------------------------------------------------------
 // Q/K: one workgroup per (64-token block, b*h, tensor); each of the 4 waves
 // takes 16 rows of the block (PairLane layout).  RoPE per pair, then (ROT ==
 // 2) the Half rotation u' = (u + w) r, w' = (u - w) r on channels
 // (i, i + L/2) of each segment through a per-wave LDS row, r = f32(1/sqrt 2);
 // ROT == 1 (Interleaved) is already merged into the tables as +pi/4.  The
-// rotated values stay in registers for the block amax, then become e4m3
-// code bytes (2 per lane and row).
+// rotated values stay in registers for the block amax, then become fp6 e2m3
+// codes, one per byte in an LDS tile, which the workgroup packs into the
+// 64-token fp6 tile and writes with coalesced 16-byte stores.
 template <int ROT, bool BF16, int D>
 __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
   using PL = PairLane<D>;
   constexpr int ITERS = 16 / PL::RPI;
   __shared__ float xch[4][PL::RPI][D];
   __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t cb[kBlock * D];   // e2m3 code per byte, [row][channel]
   const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
   const int b = bh / a.H, h = bh % a.H;
   const void* x = which ? a.k : a.q;
@@ -206,10 +227,30 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
     const int r = r0 + it * PL::RPI;
     const int c0 = amax > 0.0f ? quant_code(y[it][0], inv) : 0;
     const int c1 = amax > 0.0f ? quant_code(y[it][1], inv) : 0;
-    *reinterpret_cast<uint16_t*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + 2 * pl.j) =
-        (uint16_t)(e4m3_of_code(c0) | (e4m3_of_code(c1) << 8));
+    *reinterpret_cast<uint16_t*>(cb + r * D + 2 * pl.j) = (uint16_t)(e2m3_of_code(c0) | (e2m3_of_code(c1) << 8));
   }
   if (threadIdx.x == 0) sc[(size_t)bh * a.nblk + blk] = amax > 0.0f ? scale : 0.0f;
+  __syncthreads();
+
+  // The tile in 16-byte units: unit u < 2D is bits 0..127 of (row u % 64,
+  // group u / 64); unit 2D + v is bits 128..191 of rows 2(v % 32) and
+  // 2(v % 32) + 1 of group v / 32.  Unit u lands at byte 16 u of the tile.
+  uint8_t* tile = out + ((size_t)bh * a.Npad + (size_t)blk * kBlock) * (qk6_tile_bytes(D) / kBlock);
+  for (int u = threadIdx.x; u < 3 * D; u += 256) {
+    uint4 o;
+    if (u < 2 * D) {
+      uint32_t cw[8];
+      load_group_codes(cb + (u & 63) * D + 32 * (u >> 6), cw);
+      o = make_uint4(fp6_word<0>(cw), fp6_word<1>(cw), fp6_word<2>(cw), fp6_word<3>(cw));
+    } else {
+      const int v = u - 2 * D, g = v >> 5, r = 2 * (v & 31);
+      uint32_t c0w[8], c1w[8];
+      load_group_codes(cb + r * D + 32 * g, c0w);
+      load_group_codes(cb + (r + 1) * D + 32 * g, c1w);
+      o = make_uint4(fp6_word<4>(c0w), fp6_word<5>(c0w), fp6_word<4>(c1w), fp6_word<5>(c1w));
+    }
+    *reinterpret_cast<uint4*>(tile + 16 * u) = o;
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -100,8 +100,9 @@ ra_status ra_plan_create(const ra_shape* shape, const ra_opts* opts, ra_plan* ou
 ra_status ra_plan_destroy(ra_plan plan);
 
 /* Workspace bytes one ra_attn_fwd call of this plan needs (the INT4 codes
- * of Q/K/V, one fp8 e4m3 byte each, + scales; or the bf16 copies for the
- * bf16 path). */
+ * of Q/K/V in the matrix-instruction operand formats: Q and K as 6-bit fp6
+ * e2m3 in 64-token tiles, V as one fp8 e4m3 byte each; + scales; or the bf16
+ * copies for the bf16 path). */
 ra_status ra_plan_workspace_size(ra_plan plan, size_t* bytes);
 
 /* Same figure without a plan. */

@@ -141,6 +141,37 @@ def test_zero_queries_and_single_token(ora):
     assert np.abs(o - want).max() <= 1e-6
 
 
+def test_zero_scale_blocks(ora):
+    """Scale-0 blocks give c = 0 for their steps: an all-zero K block as the
+    ragged last block (every query's last step) and an all-zero Q block (every
+    step of those queries).  All valid keys of such a step share one grid
+    exponent, and the padded keys of the ragged step must still add nothing
+    to the row sum."""
+    w = CASES["medium"]
+    q, k, v, _ = inputs.generate(w)
+    N = w.tokens
+    nb = (N + 63) // 64
+    k[:, (nb - 1) * 64:] = 0
+    q[:, 64:128] = 0
+    pro = ora.prologue(q, k, v, w.grid, w.seg, w.theta, w.rot_id)
+    assert np.all(pro["s_k"][..., -1] == 0) and np.all(pro["s_q"][..., 1] == 0)
+    p = plan_for(w)
+    o = p.forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    want = ora.attention_full(pro)
+    err, cos = np.abs(o - want).max(), cosine(o, want)
+    say("zero-scale blocks: max|gpu-oracle| %.2e cos %.7f" % (err, cos))
+    assert err <= 2e-3 and cos >= 0.999
+    ws = p.workspace()
+    p.prologue(dev(q), dev(k), dev(v), ws)
+    for qb, kb in [(0, nb - 1), (1, nb - 1), (1, 0), (nb - 1, nb - 1)]:
+        g = p.debug_tile(ws, 0, 1, qb, kb)
+        t = ora.attention_tile(pro, 0, 1, qb, kb)
+        n = t["s_int"].shape[0]
+        assert np.array_equal(g["p_code"][:n], t["p_code"]), (qb, kb, "P")
+        assert np.array_equal(g["pv_int"][:n], t["pv_int"]), (qb, kb, "PV")
+        assert np.array_equal(g["m_after"][:n].view(np.uint32), t["m_after"].view(np.uint32)), (qb, kb, "m")
+
+
 def test_deterministic(ora):
     w = CASES["medium"]
     q, k, v, _ = inputs.generate(w)
