@@ -35,6 +35,8 @@
 //     step's PV is exact; it accumulates across steps in fp32 registers,
 //     scaled by beta only when a query's running max rises (rare after the
 //     first few steps).
+#include <type_traits>
+
 #include "ra_common.h"
 #include "ra_kernels.h"
 
@@ -479,15 +481,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   __syncthreads();
   const uint8_t* kt2 = ktiles + 2 * C::KT;      // K tile of step t + 2
   const uint8_t* vt1 = vtiles + C::VT;          // V tile of step t + 1
-#pragma nounroll
-  for (int t = 0; t + 1 < nkb; ++t, kt2 += C::KT, vt1 += C::VT) {
+  // One step; RAGGED: step t+1 is the last one and N may end inside it.
+  auto step = [&](int t, auto ragged) {
     dma.issue(t + 2 < nkb ? kt2 : nullptr, vt1, kbuf + (t & 1) * C::KT, vbuf + ((t + 1) & 1) * C::VT);
     uint32_t p[2][4];
     pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale, ptab, p, st.U);
     qk_step<D>(kbuf + ((t + 1) & 1) * C::KT, qop, s);       // S of step t+1
     pv_step<D>(vbuf + (t & 1) * C::VT, p, st.acc);
-    const int nv1 = min(kBlock, a.N - (t + 1) * kBlock);
-    if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
+    if constexpr (decltype(ragged)::value) {
+      const int nv1 = a.N - (t + 1) * kBlock;
+      if (nv1 < kBlock) mask_scores(s, nv1);
+    }
     const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
     const float m_new = fmaxf(st.m, step_max(s, cp_next));
     if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
@@ -495,7 +499,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     cp_cur = cp_next;
     wait_lds_dma();
     __syncthreads();
-  }
+    kt2 += C::KT;
+    vt1 += C::VT;
+  };
+  int t0 = 0;
+#pragma nounroll
+  for (; t0 + 2 < nkb; ++t0) step(t0, std::false_type{});
+  if (t0 + 1 < nkb) step(t0, std::true_type{});
   {
     // The last step: its V tile was copied during the step before (or
     // before the loop when nkb = 1).
