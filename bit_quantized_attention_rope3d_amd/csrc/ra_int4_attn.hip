@@ -44,6 +44,8 @@ namespace ra {
 
 constexpr int kWaves = 12;                 // waves per workgroup
 constexpr int kQTile = 32 * kWaves;        // query rows per workgroup
+constexpr int kSync = 3;                   // steps per workgroup barrier
+constexpr int kStages = 2 * kSync;         // LDS stages of K and of V tiles
 
 template <int D>
 struct Cfg {
@@ -125,11 +127,22 @@ __device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt) {
 
 // ---- K/V staging: global memory -> LDS without registers ------------------
 
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-// Buffer load with the LDS-direct bit: lane i copies `size` bytes from
-// base(rsrc) + voffset into LDS at lds + size * i (lds is wave-uniform).
-extern "C" __device__ void ra_buffer_load_lds(v4i rsrc, lds_u32* lds, int size, int voffset, int soffset,
-                                              int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+// 16-byte buffer load with the LDS-direct bit: lane i copies 16 bytes from
+// base(rsrc) + voffset into LDS at lds + 16 i (lds is wave-uniform).  It is
+// written as an instruction the compiler does not model as a store to LDS:
+// the modelled form makes the compiler wait for every copy in flight before
+// any LDS read it cannot prove disjoint from the copy's target, which here
+// is every read of the other stages.  Completion is ordered explicitly by
+// wait_lds_dma() and the workgroup barrier; no register receives data, and
+// M0 is set and used inside the statement.
+__device__ __forceinline__ void lds_copy16(v4i rsrc, const uint8_t* lds, int voffset) {
+  const uint32_t m = (uint32_t)(uintptr_t)(const lds_u8*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
 
 // Buffer descriptor over `bytes` bytes at `base` (reads past the end return 0).
 __device__ __forceinline__ v4i make_rsrc(const uint8_t* base, uint32_t bytes) {
@@ -190,9 +203,9 @@ struct TileDma {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       if (kind[j] == 1 && kt != nullptr)
-        ra_buffer_load_lds(make_rsrc(kt, Cfg<D>::KT), (lds_u32*)(kst + lds[j]), 16, off[j], 0, 0, 0);
+        lds_copy16(make_rsrc(kt, Cfg<D>::KT), kst + lds[j], off[j]);
       else if (kind[j] == 2 && vt != nullptr)
-        ra_buffer_load_lds(make_rsrc(vt, Cfg<D>::VT), (lds_u32*)(vst + lds[j]), 16, off[j], 0, 0, 0);
+        lds_copy16(make_rsrc(vt, Cfg<D>::VT), vst + lds[j], off[j]);
     }
   }
 };
@@ -424,10 +437,10 @@ __device__ __forceinline__ void state_init(State<D>& st) {
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::KT + 2 * C::VT + kPTabBytes];
-  uint8_t* const kbuf = smem;                     // 2 K stages
-  uint8_t* const vbuf = smem + 2 * C::KT;         // 2 V stages
-  uint8_t* const ptab = smem + 2 * C::KT + 2 * C::VT;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * (C::KT + C::VT) + kPTabBytes];
+  uint8_t* const kbuf = smem;                     // K stages
+  uint8_t* const vbuf = smem + kStages * C::KT;   // V stages
+  uint8_t* const ptab = smem + kStages * (C::KT + C::VT);
   ptab_build(ptab, threadIdx.x, 64 * kWaves);     // visible after the first barrier
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
@@ -457,20 +470,30 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   state_init<D>(st);
 
   // Step t: P codes of step t (S in registers), S of step t+1, P x V of step
-  // t, then the running max of step t+1 and the rescale it may need; one
-  // barrier per step.  Within a wave these run in order; the other two
-  // waves on the SIMD fill the latencies.  At the start of step t the copies
-  // of K of step t+2 and V of step t+1 into the LDS stages freed by step t-1
-  // are issued; they complete before the barrier that ends step t.
+  // t, then the running max of step t+1 and the rescale it may need.  Within
+  // a wave these run in order; the other two waves on the SIMD fill the
+  // latencies.  K/V tiles live in kStages = 2 kSync LDS stages and the
+  // workgroup barrier is taken once every kSync steps, so the waves of a
+  // SIMD drift apart within a block of steps instead of meeting in the same
+  // phase every step.  At step t each wave issues its share of the copies
+  // of K of step t + kSync + 1 (S of a step is made one step ahead) and V
+  // of step t + kSync.  A stage is rewritten only after the barrier that
+  // ends the last step reading it, and a tile is read only after the
+  // barrier that follows its copy.
   const TileDma<D, kWaves> dma;
   const uint8_t* const ktiles = a.kp + (size_t)bh * a.nblk * C::KT;
   const uint8_t* const vtiles = a.vp + (size_t)bh * a.nkb * C::VT;
-  dma.issue(ktiles, nullptr, kbuf, vbuf);
+  auto kst = [&](int t) { return kbuf + (t % kStages) * C::KT; };
+  auto vst = [&](int t) { return vbuf + (t % kStages) * C::VT; };
+  dma.issue(ktiles, nullptr, kst(0), vst(0));
   wait_lds_dma();
   __syncthreads();
-  dma.issue(nkb > 1 ? ktiles + C::KT : nullptr, vtiles, kbuf + C::KT, vbuf);
+#pragma unroll
+  for (int i = 1; i <= kSync; ++i)
+    dma.issue(i < nkb ? ktiles + i * C::KT : nullptr, i - 1 < nkb ? vtiles + (i - 1) * C::VT : nullptr,
+              kst(i), vst(i - 1));
   v16f s[2];
-  qk_step<D>(kbuf, qop, s);
+  qk_step<D>(kst(0), qop, s);
   {
     const int nv0 = min(kBlock, a.N);
     if (nv0 < kBlock) mask_scores(s, nv0);
@@ -479,41 +502,50 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   st.m = step_max(s, cp_cur);
   wait_lds_dma();
   __syncthreads();
-  const uint8_t* kt2 = ktiles + 2 * C::KT;      // K tile of step t + 2
-  const uint8_t* vt1 = vtiles + C::VT;          // V tile of step t + 1
-  // One step; RAGGED: step t+1 is the last one and N may end inside it.
-  auto step = [&](int t, auto ragged) {
-    dma.issue(t + 2 < nkb ? kt2 : nullptr, vt1, kbuf + (t & 1) * C::KT, vbuf + ((t + 1) & 1) * C::VT);
+  const uint8_t* ktn = ktiles + (kSync + 1) * C::KT;   // K tile of step t + kSync + 1
+  const uint8_t* vtn = vtiles + kSync * C::VT;         // V tile of step t + kSync
+  // One step; RAGGED: step t+1 may be the last one, with N ending inside it.
+  auto step = [&](int t, auto ragged, auto sync) {
+    dma.issue(t + kSync + 1 < nkb ? ktn : nullptr, t + kSync < nkb ? vtn : nullptr, kst(t + kSync + 1),
+              vst(t + kSync));
     uint32_t p[2][4];
     pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale, ptab, p, st.U);
-    qk_step<D>(kbuf + ((t + 1) & 1) * C::KT, qop, s);       // S of step t+1
-    pv_step<D>(vbuf + (t & 1) * C::VT, p, st.acc);
+    qk_step<D>(kst(t + 1), qop, s);       // S of step t+1
+    pv_step<D>(vst(t), p, st.acc);
     if constexpr (decltype(ragged)::value) {
       const int nv1 = a.N - (t + 1) * kBlock;
-      if (nv1 < kBlock) mask_scores(s, nv1);
+      if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
     }
     const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
     const float m_new = fmaxf(st.m, step_max(s, cp_next));
     if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
     st.m = m_new;
     cp_cur = cp_next;
-    wait_lds_dma();
-    __syncthreads();
-    kt2 += C::KT;
-    vt1 += C::VT;
+    if constexpr (decltype(sync)::value) {
+      wait_lds_dma();
+      __syncthreads();
+    }
+    ktn += C::KT;
+    vtn += C::VT;
   };
   int t0 = 0;
+  // Whole blocks in which no step is followed by the last one.
 #pragma nounroll
-  for (; t0 + 2 < nkb; ++t0) step(t0, std::false_type{});
-  if (t0 + 1 < nkb) step(t0, std::true_type{});
+  for (; t0 + kSync + 1 < nkb; t0 += kSync) {
+#pragma unroll
+    for (int i = 0; i + 1 < kSync; ++i) step(t0 + i, std::false_type{}, std::false_type{});
+    step(t0 + kSync - 1, std::false_type{}, std::true_type{});
+  }
+  // The remaining steps but the last, with a barrier after each.
+#pragma nounroll
+  for (; t0 + 1 < nkb; ++t0) step(t0, std::true_type{}, std::true_type{});
   {
-    // The last step: its V tile was copied during the step before (or
-    // before the loop when nkb = 1).
+    // The last step: its V tile is resident since the barrier before it.
     const int t = nkb - 1, nvalid = a.N - t * kBlock;
     uint32_t p[2][4];
     pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale, ptab, p, st.U);
     if (nvalid < kBlock) st.U -= padded_u(cp_cur * kPTabScale, nvalid);
-    pv_step<D>(vbuf + (t & 1) * C::VT, p, st.acc);
+    pv_step<D>(vst(t), p, st.acc);
   }
 
   // o = A s_v / L: the 1/15 of the dequantized P cancels against the
