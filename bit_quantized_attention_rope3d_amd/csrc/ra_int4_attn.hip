@@ -308,11 +308,13 @@ __device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c2, float m2
                           *reinterpret_cast<const uint16_t*>(tab + a[2 * i + 1])};
     r[i] = __builtin_bit_cast(uint32_t, v);
   }
+  uint32_t us = 0u;   // bytes: partial sums of u, at most 8 x 15 each
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     p[w >> 2][w & 3] = __builtin_amdgcn_perm(r[2 * w + 1], r[2 * w], 0x06040200u);           // e0 e1 e2 e3
-    U = __builtin_amdgcn_sad_u8(__builtin_amdgcn_perm(r[2 * w + 1], r[2 * w], 0x07050301u), 0u, U);
+    us += __builtin_amdgcn_perm(r[2 * w + 1], r[2 * w], 0x07050301u);
   }
+  U = __builtin_amdgcn_sad_u8(us, 0u, U);
 }
 
 // Padded keys of a ragged last step carry S = -inf.  With c > 0 they read
