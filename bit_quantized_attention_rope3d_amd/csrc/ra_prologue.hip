@@ -172,7 +172,6 @@ template <int ROT, bool BF16, int D>
 __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
   using PL = PairLane<D>;
   constexpr int ITERS = 16 / PL::RPI;
-  __shared__ float xch[4][PL::RPI][D];
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t cb[kBlock * D];   // e2m3 code per byte, [row][channel]
   const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
@@ -184,41 +183,54 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
   const PL pl(a.tabs);
   const int r0 = wave * 16 + pl.sub;
   GridPos gp(blk * kBlock + r0, a.tabs);
-  float* row = xch[wave][pl.sub];
 
+  // Pass 1: all rows' loads and RoPE, with no barrier in between, so every
+  // load of the wave's 16 rows (inputs and table entries) is in flight at
+  // once.
   float y[ITERS][2];
-  float mx = 0.0f;
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int n = blk * kBlock + r0 + it * PL::RPI;
     float x0 = 0.0f, x1 = 0.0f;
     if (n < a.N) load_pair<BF16>(x, (((size_t)b * a.N + n) * a.H + h) * D + 2 * pl.j, x0, x1);
-    float v0, v1;
-    pl.rope(n < a.N ? gp.axis(pl.s) : 0, x0, x1, v0, v1);
-    if (ROT == 2) {
-      row[2 * pl.j] = v0;
-      row[2 * pl.j + 1] = v1;
-      __builtin_amdgcn_wave_barrier();
-      const float r = __uint_as_float(0x3F3504F3u);
-      const int hc = (2 * pl.npair) >> 1;      // L / 2 channels
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = 2 * pl.jj + e;
-        const float own = e ? v1 : v0;
-        const bool first = i < hc;                         // own is u, partner is w
-        const float other = row[pl.off + (first ? i + hc : i - hc)];
-        const float sum = own + other;
-        const float dif = other - own;
-        y[it][e] = (first ? sum : dif) * r;
-      }
-      __builtin_amdgcn_wave_barrier();
-    } else {
-      y[it][0] = v0;
-      y[it][1] = v1;
-    }
-    mx = fmaxf(mx, fmaxf(fabsf(y[it][0]), fabsf(y[it][1])));
+    pl.rope(n < a.N ? gp.axis(pl.s) : 0, x0, x1, y[it][0], y[it][1]);
     gp.advance(PL::RPI, a.tabs);
   }
+  // Pass 2 (Half): the partner of channel i of a segment, i +- L/2, is read
+  // from the lane holding it with a cross-lane permute (no LDS allocation).
+  if (ROT == 2) {
+    const float r = __uint_as_float(0x3F3504F3u);
+    const int hc = pl.npair;                 // L / 2 channels
+    int src[2];
+    bool first[2], podd[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * pl.jj + e;
+      first[e] = i < hc;                     // own is u, partner is w
+      const int pi = first[e] ? i + hc : i - hc;
+      src[e] = pl.sub * PL::PAIRS + (pl.off >> 1) + (pi >> 1);
+      podd[e] = (pi & 1) != 0;
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      float o[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float p0 = __shfl(y[it][0], src[e], 64), p1 = __shfl(y[it][1], src[e], 64);
+        o[e] = podd[e] ? p1 : p0;
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float own = y[it][e], other = o[e];
+        const float sum = own + other;
+        const float dif = other - own;
+        y[it][e] = (first[e] ? sum : dif) * r;
+      }
+    }
+  }
+  float mx = 0.0f;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) mx = fmaxf(mx, fmaxf(fabsf(y[it][0]), fabsf(y[it][1])));
   const float amax = block_max_256(mx, red);
   const float scale = amax / 7.0f;
   const float inv = 7.0f / amax;
