@@ -129,8 +129,7 @@ __device__ __forceinline__ float xhalf_sum_f(float x) {
 
 // Segment tables for 3D RoPE: cos/sin of segment s at [pos * (seg[s]/2) + pair].
 struct RopeTabs {
-  const float* cs[3];
-  const float* sn[3];
+  const float2* csn[3];   // per segment: (cos, sin) of pos * theta_j at [pos * pairs + j]
   int seg[3];
   int off[3];
   int dims[3];   // F, H, W

@@ -184,10 +184,11 @@ ra_status device_tables(ra_plan p, ra::RopeTabs* t) {
     }
     std::vector<float> host;
     host.reserve(p->tab_floats);
-    for (int s = 0; s < 3; ++s) {
-      host.insert(host.end(), p->cs[s].begin(), p->cs[s].end());
-      host.insert(host.end(), p->sn[s].begin(), p->sn[s].end());
-    }
+    for (int s = 0; s < 3; ++s)      // (cos, sin) interleaved: one 8-byte load per pair
+      for (size_t i = 0; i < p->cs[s].size(); ++i) {
+        host.push_back(p->cs[s][i]);
+        host.push_back(p->sn[s][i]);
+      }
     if (hipMemcpy(buf, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
       hipFree(buf);
       return fail(RA_ERR_HIP, "copying RoPE tables to device %d failed", dev);
@@ -199,10 +200,8 @@ ra_status device_tables(ra_plan p, ra::RopeTabs* t) {
   const int dims[3] = {p->shape.grid_f, p->shape.grid_h, p->shape.grid_w};
   size_t o = 0;
   for (int s = 0; s < 3; ++s) {
-    t->cs[s] = buf + o;
-    o += p->cs[s].size();
-    t->sn[s] = buf + o;
-    o += p->sn[s].size();
+    t->csn[s] = reinterpret_cast<const float2*>(buf + o);
+    o += 2 * p->cs[s].size();
     t->seg[s] = p->shape.seg[s];
     t->off[s] = p->off[s];
     t->dims[s] = dims[s];

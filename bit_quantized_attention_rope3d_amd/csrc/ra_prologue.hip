@@ -55,26 +55,25 @@ struct PairLane {
   static constexpr int PAIRS = D / 2;
   static constexpr int RPI = 64 / PAIRS;   // rows per wave step
   int sub, j, s, jj, npair, off;           // row in the step, pair, segment, pair in segment, pairs in segment, channel offset
-  const float* cs;
-  const float* sn;
+  const float2* csn;
 
   __device__ __forceinline__ explicit PairLane(const RopeTabs& t) {
     const int lane = threadIdx.x & 63;
-    sub = lane / PAIRS;
-    j = lane % PAIRS;
+    sub = RPI == 1 ? 0 : lane / PAIRS;      // with one row per step the row is wave-uniform
+    j = RPI == 1 ? lane : lane % PAIRS;
     const int p1 = t.seg[0] >> 1, p2 = p1 + (t.seg[1] >> 1);
     s = (j >= p1) + (j >= p2);
     jj = j - (s == 0 ? 0 : (s == 1 ? p1 : p2));
     npair = t.seg[s] >> 1;
     off = t.off[s];
-    cs = t.cs[s];
-    sn = t.sn[s];
+    csn = t.csn[s];
   }
 
   // RoPE of (x0, x1) at axis position pos of this lane's segment: each
   // product rounded, then the difference / sum.
   __device__ __forceinline__ void rope(int pos, float x0, float x1, float& y0, float& y1) const {
-    const float c = cs[pos * npair + jj], sv = sn[pos * npair + jj];
+    const float2 cv = csn[pos * npair + jj];
+    const float c = cv.x, sv = cv.y;
     const float ac = x0 * c, bs = x1 * sv;
     const float as = x0 * sv, bc = x1 * c;
     y0 = ac - bs;
@@ -122,6 +121,18 @@ __device__ __forceinline__ void load_pair(const void* base, size_t elem_off, flo
     x0 = v.x;
     x1 = v.y;
   }
+}
+
+// fp6 e2m3 bits of the INT4 code of x: q = clamp(rint(x inv), -7, 7) as a
+// float (+0.0 turns -0 into +0), then the e2m3 fields read off its fp32
+// bits: for |q| in [1, 8) the exponent field is E + 1 and the mantissa the
+// top three fp32 mantissa bits, i.e. (bits >> 20) - 0x3F0 on the magnitude;
+// q = 0 saturates to 0.
+__device__ __forceinline__ uint32_t quant_e2m3(float x, float inv) {
+  const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(x * inv), -7.0f, 7.0f) + 0.0f;
+  const uint32_t b = __float_as_uint(q);
+  const uint32_t mag = __builtin_elementwise_sub_sat((b >> 20) & 0x7FFu, 0x3F0u);
+  return mag | ((b >> 26) & 0x20u);
 }
 
 __device__ __forceinline__ int quant_code(float x, float inv) {
@@ -179,7 +190,7 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
   const void* x = which ? a.k : a.q;
   uint8_t* out = which ? a.k_out : a.q_out;
   float* sc = which ? a.s_k : a.s_q;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const PL pl(a.tabs);
   const int r0 = wave * 16 + pl.sub;
   GridPos gp(blk * kBlock + r0, a.tabs);
@@ -198,34 +209,31 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
   }
   // Pass 2 (Half): the partner of channel i of a segment, i +- L/2, is read
   // from the lane holding it with a cross-lane permute (no LDS allocation).
+  // With L/2 even the partners of both channels of a pair sit at the same
+  // element of one lane; with L/2 odd they sit at the other element of two
+  // lanes.  Either way one permute of element 0 and one of element 1 fetch
+  // both, and u' = (u + w) r, w' = (u - w) r become fma(own, +-1, other) r.
   if (ROT == 2) {
     const float r = __uint_as_float(0x3F3504F3u);
     const int hc = pl.npair;                 // L / 2 channels
     int src[2];
-    bool first[2], podd[2];
+    float sgn[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int i = 2 * pl.jj + e;
-      first[e] = i < hc;                     // own is u, partner is w
-      const int pi = first[e] ? i + hc : i - hc;
+      const bool first = i < hc;             // own is u, partner is w
+      const int pi = first ? i + hc : i - hc;
       src[e] = pl.sub * PL::PAIRS + (pl.off >> 1) + (pi >> 1);
-      podd[e] = (pi & 1) != 0;
+      sgn[e] = first ? 1.0f : -1.0f;
     }
+    const bool odd = (hc & 1) != 0;
+    const int sa = odd ? src[1] : src[0], sb = odd ? src[0] : src[1];   // element 0 from sa, 1 from sb
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-      float o[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float p0 = __shfl(y[it][0], src[e], 64), p1 = __shfl(y[it][1], src[e], 64);
-        o[e] = podd[e] ? p1 : p0;
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float own = y[it][e], other = o[e];
-        const float sum = own + other;
-        const float dif = other - own;
-        y[it][e] = (first[e] ? sum : dif) * r;
-      }
+      const float pa = __shfl(y[it][0], sa, 64), pb = __shfl(y[it][1], sb, 64);
+      const float o0 = odd ? pb : pa, o1 = odd ? pa : pb;
+      y[it][0] = __builtin_fmaf(y[it][0], sgn[0], o0) * r;
+      y[it][1] = __builtin_fmaf(y[it][1], sgn[1], o1) * r;
     }
   }
   float mx = 0.0f;
@@ -237,9 +245,9 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int r = r0 + it * PL::RPI;
-    const int c0 = amax > 0.0f ? quant_code(y[it][0], inv) : 0;
-    const int c1 = amax > 0.0f ? quant_code(y[it][1], inv) : 0;
-    *reinterpret_cast<uint16_t*>(cb + r * D + 2 * pl.j) = (uint16_t)(e2m3_of_code(c0) | (e2m3_of_code(c1) << 8));
+    const uint32_t c0 = amax > 0.0f ? quant_e2m3(y[it][0], inv) : 0u;
+    const uint32_t c1 = amax > 0.0f ? quant_e2m3(y[it][1], inv) : 0u;
+    *reinterpret_cast<uint16_t*>(cb + r * D + 2 * pl.j) = (uint16_t)(c0 | (c1 << 8));
   }
   if (threadIdx.x == 0) sc[(size_t)bh * a.nblk + blk] = amax > 0.0f ? scale : 0.0f;
   __syncthreads();
