@@ -176,11 +176,12 @@ def schedule_pick(sched, step, n_steps, block, n_blocks) -> str:
     return "bf16" if lib().ra_schedule_pick(ctypes.byref(s), step, n_steps, block, n_blocks) else "int4"
 
 
-def pmap_device(x: torch.Tensor) -> torch.Tensor:
-    """The kernels' P map on grid exponents x (float32 CUDA tensor) -> u = code + 8."""
+def pmap_device(x: torch.Tensor, p_mode: int = 0) -> torch.Tensor:
+    """The kernels' P map on grid exponents x (float32 CUDA tensor) -> u
+    (u = code + 8 for p_mode 0, u = code for p_mode 1)."""
     x = x.contiguous()
     u = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    check(lib().ra_debug_pmap(_ptr(x), _ptr(u), x.numel(), _stream_ptr(None, x.device)),
+    check(lib().ra_debug_pmap(_ptr(x), _ptr(u), x.numel(), int(p_mode), _stream_ptr(None, x.device)),
           "ra_debug_pmap")
     return u
 

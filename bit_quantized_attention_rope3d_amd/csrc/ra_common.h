@@ -29,6 +29,7 @@ constexpr int kWave = 64;
 constexpr int kPGrid = 4755;
 constexpr float kInvPGrid = 1.0f / 4755.0f;
 constexpr float kLog2Of15 = (float)3.9068905956085187;
+constexpr float kLog2Of7 = (float)2.8073549220576042;
 
 // Code layout in the workspace, shared by the prologue (writer) and the
 // attention kernels (readers).  gfx950 has no INT4 matrix instruction, so
@@ -78,10 +79,15 @@ __host__ __device__ constexpr uint32_t e2m3_of_code(int c) {
   return (c < 0 ? 0x20u : 0u) | (uint32_t)((0x1E1C1A1814100800ull >> (8 * (c < 0 ? -c : c))) & 0xFFu);
 }
 
-// Range-optimized P code, as u = code + 8 in [0, 15], of the grid exponent
-// x (an integer-valued float <= 0), written into byte `sel` of `acc`.
-__device__ __forceinline__ uint32_t pmap_insert(float x, uint32_t sel, uint32_t acc) {
-  float w = __builtin_fmaf(x, kInvPGrid, kLog2Of15);
+// P code u = round(P p), p = 2^(x/G), of the grid exponent x (an
+// integer-valued float <= 0), written into byte `sel` of `acc`; log2p =
+// log2(P).  P = 15: range-optimized map, u = code + 8 in [0, 15]; P = 7:
+// symmetric quantization, u = code in [0, 7].  On the grid no point other
+// than p = 1/2 comes within 3e-6 (relative) of a rounding boundary of 7 p
+// either, so the same exp2 form decides every code exactly.
+__device__ __forceinline__ uint32_t pmap_insert(float x, uint32_t sel, uint32_t acc,
+                                                float log2p = kLog2Of15) {
+  float w = __builtin_fmaf(x, kInvPGrid, log2p);
   float y = __builtin_amdgcn_exp2f(w);
   return __builtin_amdgcn_cvt_pk_u8_f32(y, sel, acc);
 }

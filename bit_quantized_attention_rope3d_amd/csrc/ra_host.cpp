@@ -88,8 +88,8 @@ ra_status validate(const ra_shape* s, const ra_opts* o) {
     return fail(RA_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
   if (!(o->softmax_scale >= 0.0) || !std::isfinite(o->softmax_scale))
     return fail(RA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-  if (o->p_mode != 0)
-    return fail(RA_ERR_UNSUPPORTED, "p_mode %d not implemented (0 = range-optimized)", o->p_mode);
+  if (o->p_mode != 0 && o->p_mode != 1)
+    return fail(RA_ERR_INVALID_ARG, "p_mode %d is not 0 (range-optimized) or 1 (symmetric)", o->p_mode);
   return RA_OK;
 }
 
@@ -242,6 +242,7 @@ ra::AttnArgs attn_args(ra_plan p, uint8_t* ws, void* o) {
   a.nqt = p->lay.nqt;
   a.alpha_g = p->alpha_g;
   a.alpha = p->alpha;
+  a.p_mode = p->opts.p_mode;
   return a;
 }
 
@@ -548,10 +549,11 @@ ra_status ra_debug_tile(ra_plan p, void* ws, size_t ws_bytes, int32_t b, int32_t
   return ok();
 }
 
-ra_status ra_debug_pmap(const float* x, uint8_t* u, int64_t n, hipStream_t stream) {
+ra_status ra_debug_pmap(const float* x, uint8_t* u, int64_t n, int32_t p_mode, hipStream_t stream) {
   if (n < 0) return fail(RA_ERR_INVALID_ARG, "n must be >= 0");
   if (n > 0 && (!x || !u)) return fail(RA_ERR_INVALID_ARG, "x and u must be non-null");
-  ra::launch_pmap_probe(x, u, n, stream);
+  if (p_mode != 0 && p_mode != 1) return fail(RA_ERR_INVALID_ARG, "p_mode %d is not 0 or 1", p_mode);
+  ra::launch_pmap_probe(x, u, n, p_mode, stream);
   ra_status st = after_launch("pmap probe");
   return st == RA_OK ? ok() : st;
 }

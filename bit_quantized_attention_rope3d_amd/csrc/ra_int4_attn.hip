@@ -3,7 +3,9 @@
 // Method source: "RotateAttention: RoPE-Aware Rotation and Range Rectification
 // for INT4 Quantized Attention in Video Generation" (pith.science review):
 // abstract (INT4 Q, K, V inside FlashAttention; P = exp(QK - max QK)) and
-// Sec. 4.2 (P mapped onto the full signed INT4 range: code = round(15 p) - 8).
+// Sec. 4.2 (P mapped onto the full signed INT4 range: code = round(15 p) - 8;
+// the symmetric quantization it replaces, code = round(7 p) in [0, 7], as the
+// ablation mode p_mode = 1).
 //
 // gfx950 design
 //   * One workgroup = 12 waves = 384 query rows of one (b, h); each wave owns
@@ -118,9 +120,10 @@ __device__ __forceinline__ uint32_t e4m3_to_uint(uint32_t b) {
 // Fill the table cooperatively (threads tid, tid + nt, ...) from the exp2
 // form of the map, exact on every grid point: entry j = e4m3(u) | u << 8 for
 // u = u(-j).
-__device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt) {
+__device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt, int p_mode) {
+  const float log2p = p_mode ? kLog2Of7 : kLog2Of15;
   for (int j = tid; j < kPTabEntries; j += nt) {
-    const uint32_t u = pmap_insert(-(float)j, 0u, 0u) & 0xFFu;
+    const uint32_t u = pmap_insert(-(float)j, 0u, 0u, log2p) & 0xFFu;
     reinterpret_cast<uint16_t*>(tab)[j] = (uint16_t)(e4m3_of_uint(u) | (u << 8));
   }
 }
@@ -319,9 +322,10 @@ __device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c2, float m2
 
 // Padded keys of a ragged last step carry S = -inf.  With c > 0 they read
 // the last entry (u = 0); with c = 0 the product is NaN, which the clamp
-// turns into 0, so they read entry 0 (u = 15).  Their V codes are 0, so
-// only the row sum needs a correction: the u this lane's padded keys added.
-__device__ __forceinline__ uint32_t padded_u(float c2, int nvalid) {
+// turns into 0, so they read entry 0 (u = umax, the code of p = 1).  Their V
+// codes are 0, so only the row sum needs a correction: the u this lane's
+// padded keys added.
+__device__ __forceinline__ uint32_t padded_u(float c2, int nvalid, uint32_t umax) {
   if (c2 != 0.0f) return 0u;
   const int hf = (threadIdx.x & 63) >> 5;
   int nv = 0;
@@ -329,7 +333,7 @@ __device__ __forceinline__ uint32_t padded_u(float c2, int nvalid) {
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) nv += min(max(nvalid - (32 * mt + 8 * g + 4 * hf), 0), 4);
-  return 15u * (uint32_t)(32 - nv);
+  return umax * (uint32_t)(32 - nv);
 }
 
 // O^T += V^T P^T over the 64 keys of the step: lane half hf supplies slots
@@ -375,7 +379,9 @@ template <int D, bool DUMP>
 __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst, const uint8_t* tab,
                                           const v8i (&qop)[Cfg<D>::QC], float cq, float alpha_g,
                                           float sk, int nvalid, State<D>& st,
-                                          const TileDumpArgs* dump, int wave) {
+                                          const TileDumpArgs* dump, int wave, int p_mode) {
+  const uint32_t dump_umax = p_mode ? 7u : 15u;    // u of p = 1
+  const int zp = p_mode ? 0 : 8;                   // code = u - zp
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   v16f s[2];
@@ -387,12 +393,12 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
   st.m = m_new;
   uint32_t p[2][4];
   pmap_step(s, cp * kPTabScale, m_new * kPTabScale, tab, p, st.U);
-  if (nvalid < kBlock) st.U -= padded_u(cp * kPTabScale, nvalid);
+  if (nvalid < kBlock) st.U -= padded_u(cp * kPTabScale, nvalid, dump_umax);
   pv_step<D>(vst, p, st.acc);
 
   if (DUMP) {
     // Exact per-step integers: S, P codes (decoded from the e4m3 operand
-    // bytes), PV = sum (u - 8) vhat = sum u vhat - 8 sum vhat, running max.
+    // bytes), PV = sum (u - zp) vhat = sum u vhat - zp sum vhat, running max.
     const int qrow = wave * 32 + ln;
     v16f pv[C::DT], cs[C::DT];
     uint32_t ones[2][4];
@@ -404,7 +410,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
         if (r % 4 == 0) ones[mt][r >> 2] = 0u;
         if (key < nvalid) ones[mt][r >> 2] |= 0x38u << (8 * (r & 3));   // e4m3 1.0
         const int sv = key < nvalid ? (int)s[mt][r] : 0;
-        const int code = key < nvalid ? (int)e4m3_to_uint((p[mt][r >> 2] >> (8 * (r & 3))) & 0xFFu) - 8 : -8;
+        const int code = key < nvalid ? (int)e4m3_to_uint((p[mt][r >> 2] >> (8 * (r & 3))) & 0xFFu) - zp : -zp;
         dump->s_int[qrow * 64 + key] = sv;
         dump->p_code[qrow * 64 + key] = (int8_t)code;
       }
@@ -419,7 +425,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int d = dt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        dump->pv_int[qrow * D + d] = (int)pv[dt][r] - 8 * (int)cs[dt][r];
+        dump->pv_int[qrow * D + d] = (int)pv[dt][r] - zp * (int)cs[dt][r];
       }
     if (hf == 0) dump->m_after[qrow] = st.m;
   }
@@ -443,7 +449,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   uint8_t* const kbuf = smem;                     // K stages
   uint8_t* const vbuf = smem + kStages * C::KT;   // V stages
   uint8_t* const ptab = smem + kStages * (C::KT + C::VT);
-  ptab_build(ptab, threadIdx.x, 64 * kWaves);     // visible after the first barrier
+  ptab_build(ptab, threadIdx.x, 64 * kWaves, a.p_mode);     // visible after the first barrier
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of (head, query-tile) ids.
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     const int t = nkb - 1, nvalid = a.N - t * kBlock;
     uint32_t p[2][4];
     pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale, ptab, p, st.U);
-    if (nvalid < kBlock) st.U -= padded_u(cp_cur * kPTabScale, nvalid);
+    if (nvalid < kBlock) st.U -= padded_u(cp_cur * kPTabScale, nvalid, a.p_mode ? 7u : 15u);
     pv_step<D>(vst(t), p, st.acc);
   }
 
@@ -589,7 +595,7 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::KT + C::VT + kPTabBytes];
   uint8_t* const ptab = smem + C::KT + C::VT;
-  ptab_build(ptab, threadIdx.x, 128);
+  ptab_build(ptab, threadIdx.x, 128, a.p_mode);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const int bh = t.bh;
   const int q0 = t.q_blk * kBlock + wave * 32;
@@ -607,9 +613,9 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
     const int nvalid = min(kBlock, a.N - kb * kBlock);
     const float sk = a.s_k[(size_t)bh * a.nblk + kb];
     if (kb == t.kv_blk)
-      tile_step<D, true>(smem, smem + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, &t, wave);
+      tile_step<D, true>(smem, smem + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, &t, wave, a.p_mode);
     else
-      tile_step<D, false>(smem, smem + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave);
+      tile_step<D, false>(smem, smem + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave, a.p_mode);
     __syncthreads();
   }
 }
@@ -617,9 +623,9 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
 // The kernels' P map on grid exponents x <= 0: the same table and index
 // arithmetic, with S = x, c = 1, m = 0 (so v = -x exactly).
 __global__ __launch_bounds__(256) void k_pmap_probe(const float* __restrict__ x, uint8_t* __restrict__ u,
-                                                    int64_t n) {
+                                                    int64_t n, int p_mode) {
   __shared__ __attribute__((aligned(16))) uint8_t tab[kPTabBytes];
-  ptab_build(tab, threadIdx.x, 256);
+  ptab_build(tab, threadIdx.x, 256, p_mode);
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
@@ -653,10 +659,10 @@ void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipS
   else k_int4_tile_dump<64><<<1, 128, 0, st>>>(a, t);
 }
 
-void launch_pmap_probe(const float* x, uint8_t* u, int64_t n, hipStream_t st) {
+void launch_pmap_probe(const float* x, uint8_t* u, int64_t n, int p_mode, hipStream_t st) {
   if (n <= 0) return;
   const int64_t blocks = (n + 255) / 256;
-  k_pmap_probe<<<(unsigned)(blocks < 1024 ? blocks : 1024), 256, 0, st>>>(x, u, n);
+  k_pmap_probe<<<(unsigned)(blocks < 1024 ? blocks : 1024), 256, 0, st>>>(x, u, n, p_mode);
 }
 
 void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {

@@ -43,6 +43,7 @@ struct AttnArgs {
   int N, H, Npad, nblk, nkb, nqt;
   float alpha_g;      // f32(log2(e) * softmax_scale * kPGrid)   (int4 path)
   float alpha;        // f32(log2(e) * softmax_scale)            (bf16 path)
+  int p_mode;         // 0: range-optimized P (u = round(15 p), code u - 8); 1: symmetric (u = code = round(7 p))
 };
 
 struct TileDumpArgs {
@@ -59,7 +60,7 @@ void launch_bf16_prologue(const QKPrologueArgs& qa, const VQuantArgs& vq, int D,
                           hipStream_t st);
 void launch_int4_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
 void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipStream_t st);
-void launch_pmap_probe(const float* x, uint8_t* u, int64_t n, hipStream_t st);
+void launch_pmap_probe(const float* x, uint8_t* u, int64_t n, int p_mode, hipStream_t st);
 void launch_bf16_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
 void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 

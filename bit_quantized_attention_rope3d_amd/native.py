@@ -67,7 +67,7 @@ _SIGS = {
                                   c_void, c_void, c_void, c_void, c_void, c_void, c_void]),
     "ra_debug_tile": (c_i32, [c_void, c_void, c_size, c_i32, c_i32, c_i32, c_i32,
                               c_void, c_void, c_void, c_void, c_void]),
-    "ra_debug_pmap": (c_i32, [c_void, c_void, c_i64, c_void]),
+    "ra_debug_pmap": (c_i32, [c_void, c_void, c_i64, c_i32, c_void]),
     "ra_debug_tables": (c_i32, [c_void, c_i32, c_void, c_void]),
     "ra_copy": (c_i32, [c_void, c_void, c_size, c_void]),
 }

@@ -71,8 +71,12 @@ typedef struct {
 } ra_shape;
 
 /* Options.  rope_theta: RoPE base (10000 in the pages' models; > 0).
- * softmax_scale: 0 selects 1/sqrt(head_dim).  p_mode: 0 = range-optimized P
- * (the only mode implemented; other values return RA_ERR_UNSUPPORTED). */
+ * softmax_scale: 0 selects 1/sqrt(head_dim).  p_mode selects the INT4 map of
+ * the attention probabilities p in [0, 1] ([RA] Sec. 4.2): 0 = range-optimized
+ * (default; code = round(15 p) - 8, the full signed range [-8, 7]), 1 =
+ * symmetric quantization, the baseline the pages improve on (code = round(7 p)
+ * in [0, 7], half of the codes unused); other values return
+ * RA_ERR_INVALID_ARG.  The bf16 path ignores it. */
 typedef struct {
   int32_t rot;        /* ra_rot */
   int32_t prec;       /* ra_prec */
@@ -167,9 +171,11 @@ ra_status ra_debug_tile(ra_plan plan, void* workspace, size_t workspace_bytes,
                         int32_t* s_int, int8_t* p_codes, int32_t* pv_int, float* m_after,
                         hipStream_t stream);
 
-/* Evaluate the kernels' P map on n grid exponents: x (device, f32) -> u = code
- * + 8 (device, u8).  Enqueue only. */
-ra_status ra_debug_pmap(const float* x, uint8_t* u, int64_t n, hipStream_t stream);
+/* Evaluate the kernels' P map of mode p_mode (see ra_opts) on n grid
+ * exponents: x (device, f32) -> u (device, u8): u = code + 8 in [0, 15] for
+ * p_mode 0, u = code in [0, 7] for p_mode 1.  p_mode outside {0, 1} returns
+ * RA_ERR_INVALID_ARG.  Enqueue only. */
+ra_status ra_debug_pmap(const float* x, uint8_t* u, int64_t n, int32_t p_mode, hipStream_t stream);
 
 /* Host copy of the plan's binary32 RoPE table of segment `seg` (0 frame,
  * 1 height, 2 width): cos and sin, each [positions, seg_len/2]. */

@@ -25,7 +25,7 @@ BLOCK = 64
 __all__ = [
     "build", "lib", "ROT_NONE", "ROT_INTERLEAVED", "ROT_HALF", "ROT_NAMES",
     "BLOCK", "pgrid", "bf16_bits_to_f32", "as_f32", "rope_table", "rope_rotate",
-    "quant_qk", "quant_v", "prologue", "pmap_thresholds", "pmap",
+    "quant_qk", "quant_v", "prologue", "pmap_thresholds", "pmap", "P_SCALE", "P_ZERO",
     "attention_rows", "attention_tile", "attention_full", "schedule_full_precision",
     "set_threads", "get_threads",
 ]
@@ -61,11 +61,14 @@ def lib():
             L.ora_quant_v.argtypes = [P, i32, i32, i32, i32, P, P]
             L.ora_pmap_thresholds.argtypes = [i32, P]
             L.ora_pmap.argtypes = [P, ctypes.c_int64, P]
-            L.ora_attention_head.argtypes = [P, P, P, P, P, P, i32, i32, f64,
+            L.ora_pmap_thresholds_p.argtypes = [i32, i32, P]
+            L.ora_pmap_p.argtypes = [P, ctypes.c_int64, i32, P]
+            L.ora_attention_head.argtypes = [P, P, P, P, P, P, i32, i32, f64, i32,
                                              P, i32, P, P, i32, P, P, P, P]
             L.ora_schedule_full_precision.argtypes = [i32] * 8
             for name in ("ora_rope_table", "ora_rope_rotate", "ora_quant_qk",
                          "ora_quant_v", "ora_pmap_thresholds", "ora_pmap",
+                         "ora_pmap_thresholds_p", "ora_pmap_p",
                          "ora_attention_head", "ora_schedule_full_precision"):
                 getattr(L, name).restype = i32
             _lib = L
@@ -158,17 +161,21 @@ def prologue(q, k, v, grid, seg, theta=10000.0, rot=ROT_HALF):
     return dict(q_codes=qc, s_q=sq, k_codes=kc, s_k=sk, v_codes=vc, s_v=sv)
 
 
-def pmap_thresholds(G: int | None = None) -> np.ndarray:
-    tau = np.empty(15, np.int32)
-    _check(lib().ora_pmap_thresholds(int(G or pgrid()), _p(tau)), "pmap_thresholds")
+P_SCALE = {0: 15, 1: 7}        # p_mode 0: range-optimized; 1: symmetric
+P_ZERO = {0: 8, 1: 0}          # zero-point: code = u - P_ZERO[p_mode]
+
+
+def pmap_thresholds(G: int | None = None, p_mode: int = 0) -> np.ndarray:
+    tau = np.empty(P_SCALE[p_mode], np.int32)
+    _check(lib().ora_pmap_thresholds_p(int(G or pgrid()), int(p_mode), _p(tau)), "pmap_thresholds")
     return tau
 
 
-def pmap(x) -> np.ndarray:
-    """u = code + 8 for grid exponents x (binary32 values)."""
+def pmap(x, p_mode: int = 0) -> np.ndarray:
+    """u = code + zero-point for grid exponents x (binary32 values)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     u = np.empty(x.shape, np.uint8)
-    _check(lib().ora_pmap(_p(x), x.size, _p(u)), "pmap")
+    _check(lib().ora_pmap_p(_p(x), x.size, int(p_mode), _p(u)), "pmap")
     return u
 
 
@@ -178,7 +185,7 @@ def _head(pro, b, h):
             np.ascontiguousarray(pro["v_codes"][b, h]), np.ascontiguousarray(pro["s_v"][b, h]))
 
 
-def attention_rows(pro, b, h, rows, softmax_scale=None, with_m=False):
+def attention_rows(pro, b, h, rows, softmax_scale=None, with_m=False, p_mode=0):
     """Oracle output rows (binary64) of head (b, h) for query indices `rows`."""
     qc, sq, kc, sk, vc, sv = _head(pro, b, h)
     N, D = qc.shape
@@ -187,12 +194,12 @@ def attention_rows(pro, b, h, rows, softmax_scale=None, with_m=False):
     o = np.empty((rows.size, D), np.float64)
     m = np.empty(rows.size, np.float32)
     _check(lib().ora_attention_head(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), N, D,
-                                    scale, _p(rows), rows.size, _p(o), _p(m), -1,
+                                    scale, int(p_mode), _p(rows), rows.size, _p(o), _p(m), -1,
                                     None, None, None, None), "attention_head")
     return (o, m) if with_m else o
 
 
-def attention_tile(pro, b, h, q_blk, kv_blk, softmax_scale=None):
+def attention_tile(pro, b, h, q_blk, kv_blk, softmax_scale=None, p_mode=0):
     """Tile dump after key step kv_blk for the 64 query rows of q_blk.
 
     Rows past N are absent; returns dict of s_int [r,64], p_code [r,64],
@@ -209,20 +216,20 @@ def attention_tile(pro, b, h, q_blk, kv_blk, softmax_scale=None):
     pv = np.zeros((n, D), np.int32)
     m_after = np.zeros(n, np.float32)
     _check(lib().ora_attention_head(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), N, D,
-                                    scale, _p(rows), n, _p(o), None, int(kv_blk),
+                                    scale, int(p_mode), _p(rows), n, _p(o), None, int(kv_blk),
                                     _p(s_int), _p(p_code), _p(pv), _p(m_after)),
            "attention_tile")
     return dict(s_int=s_int, p_code=p_code, pv_int=pv, m_after=m_after)
 
 
-def attention_full(pro, softmax_scale=None):
+def attention_full(pro, softmax_scale=None, p_mode=0):
     """Oracle output [B, N, H, D] (binary64) for every row of every head."""
     B, H, N, D = pro["q_codes"].shape
     out = np.empty((B, N, H, D), np.float64)
     rows = np.arange(N, dtype=np.int32)
     for b in range(B):
         for h in range(H):
-            out[b, :, h, :] = attention_rows(pro, b, h, rows, softmax_scale)
+            out[b, :, h, :] = attention_rows(pro, b, h, rows, softmax_scale, p_mode=p_mode)
     return out
 
 

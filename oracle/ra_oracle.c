@@ -11,7 +11,9 @@
  *        Quantized Attention in Video Generation" -- pith.science review page:
  *        abstract, Sec. 3 / Fig. 2 (3D RoPE segments), Sec. 4.1 / Fig. 3
  *        (Interleaved and Half rotations, H2 blocks, orthogonality argument),
- *        Sec. 4.2 (range-optimized P: scale 15, zero-point -8), Sec. 5.1
+ *        Sec. 4.2 (range-optimized P: scale 15, zero-point -8; the symmetric
+ *        P quantization it replaces, which leaves half of the INT4 codes
+ *        unused, as the ablation mode), Sec. 5.1
  *        (FP16 step/block fallback), free-parameter ledger.
  *  [PARO] "PAROAttention" review page -- 64-token blocks aligned with the
  *        FlashAttention tile (precedent for the Q/K quantization block).
@@ -240,37 +242,50 @@ int ora_quant_v(const float *v, int B, int N, int H, int D,
  * code = round(15 p) - 8, p = 2^(x/G) with x the integer exponent on the grid
  * of G steps per log2 unit.  Rounding is half-up; u = code + 8 in [0, 15].
  * Written as a count of thresholds: u = #{k in 0..14 : x >= tau_k}, where
- * tau_k is the smallest integer with 15 * 2^(tau_k/G) >= k + 1/2.           */
-int ora_pmap_thresholds(int G, int32_t *tau)
+ * tau_k is the smallest integer with 15 * 2^(tau_k/G) >= k + 1/2.
+ *
+ * Symmetric P quantization (the baseline [RA] Sec. 4.2 replaces: P >= 0 on
+ * a symmetric INT4 grid uses only the codes 0..7): code = u = round(7 p) in
+ * [0, 7], zero-point 0; thresholds as above with 7 in place of 15.
+ * ora_pmap_scale(mode) is the scale: 15 for mode 0, 7 for mode 1.          */
+static int pmap_scale(int p_mode) { return p_mode ? 7 : 15; }
+
+int ora_pmap_thresholds_p(int G, int p_mode, int32_t *tau)
 {
-    if (G < 1) return -1;
-    for (int k = 0; k < 15; ++k) {
+    if (G < 1 || (p_mode != 0 && p_mode != 1)) return -1;
+    const int P = pmap_scale(p_mode);
+    for (int k = 0; k < P; ++k) {
         long double target = (long double)k + 0.5L;
-        long double t = log2l((long double)(2 * k + 1) / 30.0L) * (long double)G;
+        long double t = log2l((long double)(2 * k + 1) / (2.0L * P)) * (long double)G;
         long x = (long)ceill(t);
-        while (15.0L * exp2l((long double)x / G) < target) ++x;
-        while (15.0L * exp2l((long double)(x - 1) / G) >= target) --x;
+        while ((long double)P * exp2l((long double)x / G) < target) ++x;
+        while ((long double)P * exp2l((long double)(x - 1) / G) >= target) --x;
         tau[k] = (int32_t)x;
     }
     return 0;
 }
 
-static int pmap_u(float x, const int32_t *tau)
+int ora_pmap_thresholds(int G, int32_t *tau) { return ora_pmap_thresholds_p(G, 0, tau); }
+
+static int pmap_u(float x, const int32_t *tau, int P)
 {
     int u = 0;
-    for (int k = 0; k < 15; ++k)
+    for (int k = 0; k < P; ++k)
         if (x >= (float)tau[k]) ++u;
     return u;
 }
 
 /* Vectorised form for tests: u[i] = map(x[i]) with the oracle's grid. */
-int ora_pmap(const float *x, int64_t n, uint8_t *u)
+int ora_pmap_p(const float *x, int64_t n, int p_mode, uint8_t *u)
 {
     int32_t tau[15];
-    ora_pmap_thresholds(ORA_PGRID, tau);
-    for (int64_t i = 0; i < n; ++i) u[i] = (uint8_t)pmap_u(x[i], tau);
+    if (ora_pmap_thresholds_p(ORA_PGRID, p_mode, tau)) return -1;
+    const int P = pmap_scale(p_mode);
+    for (int64_t i = 0; i < n; ++i) u[i] = (uint8_t)pmap_u(x[i], tau, P);
     return 0;
 }
+
+int ora_pmap(const float *x, int64_t n, uint8_t *u) { return ora_pmap_p(x, n, 0, u); }
 
 /* Smallest binary32 value >= the exact product s * c (s integer, |s| < 2^24). */
 static float mul_round_up(int32_t s, float c)
@@ -293,30 +308,32 @@ static float mul_round_up(int32_t s, float c)
  *   step max   m_t = smallest f32 >= max_j(S_j) * c;  m = max(m, m_t)
  *   exponent   x_j = RNE(f32(S_j c - m))  (single rounding of the exact value)
  *   P code     u_j = #{k : x_j >= tau_k}  in [0, 15]; code = u - 8
+ *              (p_mode 1, symmetric: u_j in [0, 7], code = u, zero-point 0)
  *   sums       U = sum_j u_j;  num_c = sum_j u_j vhat_jc;
  *              PV_c = sum_j code_j vhat_jc = num_c - 8 sum_j vhat_jc
  *   float path (binary64):  beta = 2^((m_old - m)/G),
  *              A = A beta + num,  L = L beta + U,  o = A s_v / L.
- * The dequantized P is u/15, so the 1/15 cancels in A/L: the row is
+ * The dequantized P is u/15 (u/7), so the scale cancels in A/L: the row is
  * normalised by the sum of its quantized probabilities.
  *
  * qc, kc, vc: [N, D] int8 codes of this (b, h); sq, sk: [ceil(N/64)];
  * sv: [D].  rows: nrows query indices; o: [nrows, D] binary64.
  * m_out (optional): final running max per selected row (binary32).
  * Tile dump (optional, dbg_kb >= 0): for selected rows, after key step dbg_kb,
- * s_int[r*64 + j], p_code[r*64 + j] (-8 for keys >= N), pv_int[r*D + c],
+ * s_int[r*64 + j], p_code[r*64 + j] (-zero-point for keys >= N), pv_int[r*D + c],
  * m_after[r], indexed by r = position of the row in `rows`.                 */
 int ora_attention_head(const int8_t *qc, const float *sq,
                        const int8_t *kc, const float *sk,
                        const int8_t *vc, const float *sv,
-                       int N, int D, double softmax_scale,
+                       int N, int D, double softmax_scale, int p_mode,
                        const int32_t *rows, int nrows, double *o, float *m_out,
                        int dbg_kb, int32_t *s_int, int8_t *p_code,
                        int32_t *pv_int, float *m_after)
 {
     if (D > ORA_MAX_D || N < 1) return -1;
     int32_t tau[15];
-    ora_pmap_thresholds(ORA_PGRID, tau);
+    if (ora_pmap_thresholds_p(ORA_PGRID, p_mode, tau)) return -1;
+    const int P = pmap_scale(p_mode), zp = p_mode ? 0 : 8;
     const float alphaG = (float)(M_LOG2E * softmax_scale * (double)ORA_PGRID);
     int nkb = (N + ORA_BLOCK - 1) / ORA_BLOCK;
 
@@ -353,7 +370,7 @@ int ora_attention_head(const int8_t *qc, const float *sq,
             for (int j = 0; j < nj; ++j) {
                 float dlt = fmaf((float)S[j], c, -mnew);
                 float x = rintf(dlt);
-                u[j] = pmap_u(x, tau);
+                u[j] = pmap_u(x, tau, P);
                 U += u[j];
                 const int8_t *vj = vc + (size_t)(j0 + j) * D;
                 for (int c2 = 0; c2 < D; ++c2) num[c2] += (int64_t)u[j] * vj[c2];
@@ -367,13 +384,13 @@ int ora_attention_head(const int8_t *qc, const float *sq,
                 for (int j = 0; j < ORA_BLOCK; ++j) {
                     if (s_int) s_int[(size_t)r * ORA_BLOCK + j] = j < nj ? S[j] : 0;
                     if (p_code) p_code[(size_t)r * ORA_BLOCK + j] =
-                        (int8_t)(j < nj ? u[j] - 8 : -8);
+                        (int8_t)(j < nj ? u[j] - zp : -zp);
                 }
                 if (pv_int)
                     for (int c2 = 0; c2 < D; ++c2) {
                         int64_t acc = 0;
                         for (int j = 0; j < nj; ++j)
-                            acc += (int64_t)(u[j] - 8) * vc[(size_t)(j0 + j) * D + c2];
+                            acc += (int64_t)(u[j] - zp) * vc[(size_t)(j0 + j) * D + c2];
                         pv_int[(size_t)r * D + c2] = (int32_t)acc;
                     }
                 if (m_after) m_after[r] = m;

@@ -80,7 +80,8 @@ def test_shape_validation(L, kw, code):
     (dict(out_dtype=-1), "RA_ERR_DTYPE"),
     (dict(rope_theta=0.0), "RA_ERR_INVALID_ARG"),
     (dict(softmax_scale=-1.0), "RA_ERR_INVALID_ARG"),
-    (dict(p_mode=1), "RA_ERR_UNSUPPORTED"),
+    (dict(p_mode=2), "RA_ERR_INVALID_ARG"),
+    (dict(p_mode=-1), "RA_ERR_INVALID_ARG"),
 ])
 def test_opts_validation(L, kw, code):
     rc, h = _create(native.make_shape(1, 2, 64, (2, 4, 4), (24, 20, 20)), native.make_opts(**kw))

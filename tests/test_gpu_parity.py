@@ -43,18 +43,20 @@ def _prep(ora, w):
     return q, k, v, pro
 
 
-def test_pmap_exhaustive(ora):
+@pytest.mark.parametrize("p_mode", [0, 1])
+def test_pmap_exhaustive(ora, p_mode):
     """Every grid exponent the kernels can produce (x <= 0) down to -2^23,
-    plus far-negative extremes, through the kernels' P-map device function."""
+    plus far-negative extremes, through the kernels' P-map table (range-
+    optimized and symmetric maps)."""
     G = ora.pgrid()
     x = np.arange(-(1 << 23), 1, dtype=np.int64).astype(np.float32)
     extra = np.array([-np.inf, -3.0e38, -1.0e30, -2.0 ** 24, -2.0 ** 24 - 2, -1e9, -G, -G + 1, 0.0],
                      np.float32)
     x = np.concatenate([x, extra])
-    u_gpu = pmap_device(dev(x)).cpu().numpy()
-    u_ora = ora.pmap(x)
+    u_gpu = pmap_device(dev(x), p_mode).cpu().numpy()
+    u_ora = ora.pmap(x, p_mode=p_mode)
     bad = np.nonzero(u_gpu != u_ora)[0]
-    say("pmap exhaustive: %d values, %d mismatches" % (x.size, bad.size))
+    say("pmap exhaustive (p_mode %d): %d values, %d mismatches" % (p_mode, x.size, bad.size))
     assert bad.size == 0, (x[bad[:10]], u_gpu[bad[:10]], u_ora[bad[:10]])
 
 
@@ -141,7 +143,8 @@ def test_zero_queries_and_single_token(ora):
     assert np.abs(o - want).max() <= 1e-6
 
 
-def test_zero_scale_blocks(ora):
+@pytest.mark.parametrize("p_mode", [0, 1])
+def test_zero_scale_blocks(ora, p_mode):
     """Scale-0 blocks give c = 0 for their steps: an all-zero K block as the
     ragged last block (every query's last step) and an all-zero Q block (every
     step of those queries).  All valid keys of such a step share one grid
@@ -155,17 +158,17 @@ def test_zero_scale_blocks(ora):
     q[:, 64:128] = 0
     pro = ora.prologue(q, k, v, w.grid, w.seg, w.theta, w.rot_id)
     assert np.all(pro["s_k"][..., -1] == 0) and np.all(pro["s_q"][..., 1] == 0)
-    p = plan_for(w)
+    p = plan_for(w, p_mode=p_mode)
     o = p.forward(dev(q), dev(k), dev(v)).cpu().numpy()
-    want = ora.attention_full(pro)
+    want = ora.attention_full(pro, p_mode=p_mode)
     err, cos = np.abs(o - want).max(), cosine(o, want)
-    say("zero-scale blocks: max|gpu-oracle| %.2e cos %.7f" % (err, cos))
+    say("zero-scale blocks (p_mode %d): max|gpu-oracle| %.2e cos %.7f" % (p_mode, err, cos))
     assert err <= 2e-3 and cos >= 0.999
     ws = p.workspace()
     p.prologue(dev(q), dev(k), dev(v), ws)
     for qb, kb in [(0, nb - 1), (1, nb - 1), (1, 0), (nb - 1, nb - 1)]:
         g = p.debug_tile(ws, 0, 1, qb, kb)
-        t = ora.attention_tile(pro, 0, 1, qb, kb)
+        t = ora.attention_tile(pro, 0, 1, qb, kb, p_mode=p_mode)
         n = t["s_int"].shape[0]
         assert np.array_equal(g["p_code"][:n], t["p_code"]), (qb, kb, "P")
         assert np.array_equal(g["pv_int"][:n], t["pv_int"]), (qb, kb, "PV")
@@ -207,3 +210,36 @@ def test_bf16_path_vs_fp64(ora, case):
     say("bf16 path %s: vs fp64 on bf16 inputs max %.3e cos %.7f | vs exact fp64 max %.3e cos %.6f"
         % (case, err, cos, np.abs(o - exact).max(), cosine(o, exact)))
     assert cos >= 0.9999 and err <= 2e-2
+
+
+# ---- symmetric P mode (p_mode = 1) ------------------------------------------
+
+@pytest.mark.parametrize("case", ["tiny", "small", "small_d64", "medium"])
+def test_symmetric_mode_matches_oracle(ora, case):
+    """p_mode 1 (code = round(7 p), the baseline of [RA] Sec. 4.2) through the
+    same kernels: tiles bit-exact, output within tolerance of the oracle's
+    float path; errors of both maps against fp64 attention are printed."""
+    w = CASES[case]
+    q, k, v, pro = _prep(ora, w)
+    p = plan_for(w, p_mode=1)
+    ws = p.workspace()
+    p.prologue(dev(q), dev(k), dev(v), ws)
+    N = w.tokens
+    nb = (N + 63) // 64
+    for b in range(w.batch):
+        for h in sorted({0, w.heads - 1}):
+            for qb, kb in sorted({(0, 0), (nb - 1, nb - 1), (0, nb - 1), (nb // 2, nb // 2)}):
+                g = p.debug_tile(ws, b, h, qb, kb)
+                t = ora.attention_tile({kk: vv[b:b + 1] for kk, vv in pro.items()}, 0, h, qb, kb, p_mode=1)
+                n = t["s_int"].shape[0]
+                assert np.array_equal(g["p_code"][:n], t["p_code"]), (case, b, h, qb, kb, "P")
+                assert np.array_equal(g["pv_int"][:n], t["pv_int"]), (case, b, h, qb, kb, "PV")
+                assert np.array_equal(g["m_after"][:n].view(np.uint32), t["m_after"].view(np.uint32))
+    o = p.forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    want = ora.attention_full(pro, p_mode=1)
+    err, cos = np.abs(o - want).max(), cosine(o, want)
+    ref = ref_fp64.reference_output(ora.as_f32(q), ora.as_f32(k), ora.as_f32(v), w.grid, w.seg, w.theta)
+    o0 = plan_for(w).forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    say("symmetric %s: max|gpu-oracle| %.2e cos %.7f | vs fp64: symmetric mean %.3e, range-optimized mean %.3e"
+        % (case, err, cos, np.abs(o - ref).mean(), np.abs(o0 - ref).mean()))
+    assert err <= 2e-3 and cos >= 0.999

@@ -174,3 +174,65 @@ def test_close_to_full_precision_on_well_conditioned_data(ora, rot):
     want = ref.reference_output(q, k, v, grid, seg)
     cos = (o * want).sum() / np.sqrt((o * o).sum() * (want * want).sum())
     assert cos > 0.9
+
+
+# ---- symmetric P mode (p_mode = 1: code = round(7 p) in [0, 7]) ------------
+
+def test_symmetric_zero_queries_give_channel_means(ora):
+    """Q = 0: every p is 1, code 7 for every key; the scale cancels in A/L, so
+    the output is again the mean of the dequantized V rows."""
+    rng = np.random.default_rng(11)
+    N, D = 150, 64
+    vc = rng.integers(-7, 8, size=(N, D))
+    sv = rng.uniform(0.5, 2.0, D).astype(np.float32)
+    pro = _pro(np.zeros((N, D), int), rng.integers(-7, 8, size=(N, D)), vc, sv=sv)
+    o = ora.attention_rows(pro, 0, 0, np.arange(N), p_mode=1)
+    want = sv.astype(np.float64) * vc.mean(axis=0)
+    assert np.allclose(o, want[None, :], rtol=1e-12, atol=1e-12)
+    t = ora.attention_tile(pro, 0, 0, 0, 2, p_mode=1)
+    nk = N - 128
+    assert np.all(t["p_code"][:, :nk] == 7) and np.all(t["p_code"][:, nk:] == 0)
+
+
+def test_symmetric_tile_codes_agree_with_the_optimized_ones(ora):
+    """Both modes round the same p of every key (same scores, running max and
+    grid exponent): u7 = round(7 p) and u15 = round(15 p) must bracket a common
+    p, i.e. the intervals [(u7 - 1/2)/7, (u7 + 1/2)/7] and
+    [(u15 - 1/2)/15, (u15 + 1/2)/15] meet.  PV is the code matrix times V."""
+    rng = np.random.default_rng(12)
+    N, D = 200, 128
+    qc = rng.integers(-7, 8, size=(N, D))
+    kc = rng.integers(-7, 8, size=(N, D))
+    vc = rng.integers(-7, 8, size=(N, D))
+    pro = _pro(qc, kc, vc, sq=rng.uniform(0.001, 0.01, 4), sk=rng.uniform(0.001, 0.01, 4))
+    for kb in range(4):
+        t1 = ora.attention_tile(pro, 0, 0, 1, kb, p_mode=1)
+        t0 = ora.attention_tile(pro, 0, 0, 1, kb)
+        j0, j1 = kb * 64, min(N, kb * 64 + 64)
+        assert np.array_equal(t1["s_int"], t0["s_int"])
+        assert np.array_equal(t1["m_after"].view(np.uint32), t0["m_after"].view(np.uint32))
+        u7 = t1["p_code"][:, : j1 - j0].astype(np.float64)
+        u15 = t0["p_code"][:, : j1 - j0].astype(np.float64) + 8
+        assert u7.min() >= 0 and u7.max() <= 7
+        lo = np.maximum((u7 - 0.5) / 7, (u15 - 0.5) / 15)
+        hi = np.minimum((u7 + 0.5) / 7, (u15 + 0.5) / 15)
+        assert np.all(lo <= hi + 1e-12)
+        assert np.all(t1["p_code"][:, j1 - j0:] == 0)
+        assert np.array_equal(t1["pv_int"], t1["p_code"][:, : j1 - j0].astype(np.int64) @ vc[j0:j1])
+
+
+def test_range_optimized_map_is_closer_to_full_precision(ora):
+    """[RA] Sec. 4.2's claim on synthetic data: with the rest of the path
+    fixed, the full-range P map gives a smaller error against fp64 attention
+    than the symmetric map."""
+    rng = np.random.default_rng(13)
+    grid, seg = (2, 6, 16), (24, 20, 20)
+    N, H, D = 192, 2, 64
+    q = rng.standard_normal((1, N, H, D)).astype(np.float32)
+    k = rng.standard_normal((1, N, H, D)).astype(np.float32)
+    v = rng.standard_normal((1, N, H, D)).astype(np.float32)
+    pro = ora.prologue(q, k, v, grid, seg, 10000.0, 2)
+    want = ref.reference_output(q, k, v, grid, seg)
+    e0 = np.abs(ora.attention_full(pro) - want).mean()
+    e1 = np.abs(ora.attention_full(pro, p_mode=1) - want).mean()
+    assert e0 < e1
