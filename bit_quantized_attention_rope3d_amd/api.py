@@ -36,7 +36,7 @@ class Plan:
 
     def __init__(self, batch, heads, head_dim, grid, seg, rot="half", prec="int4",
                  in_dtype="bf16", out_dtype="f32", rope_theta=10000.0, softmax_scale=0.0,
-                 p_mode=0):
+                 p_mode=0, v_hadamard=0):
         self.batch, self.heads, self.head_dim = int(batch), int(heads), int(head_dim)
         self.grid = tuple(int(x) for x in grid)
         self.seg = tuple(int(x) for x in seg)
@@ -44,7 +44,7 @@ class Plan:
         self.tokens = self.grid[0] * self.grid[1] * self.grid[2]
         self._shape = native.make_shape(self.batch, self.heads, self.head_dim, self.grid, self.seg)
         self._opts = native.make_opts(rot, prec, in_dtype, out_dtype, rope_theta, softmax_scale,
-                                      p_mode)
+                                      p_mode, v_hadamard)
         h = ctypes.c_void_p()
         check(lib().ra_plan_create(ctypes.byref(self._shape), ctypes.byref(self._opts),
                                    ctypes.byref(h)), "ra_plan_create")

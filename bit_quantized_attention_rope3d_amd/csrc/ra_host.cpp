@@ -90,6 +90,8 @@ ra_status validate(const ra_shape* s, const ra_opts* o) {
     return fail(RA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   if (o->p_mode != 0 && o->p_mode != 1)
     return fail(RA_ERR_INVALID_ARG, "p_mode %d is not 0 (range-optimized) or 1 (symmetric)", o->p_mode);
+  if (o->v_hadamard != 0 && o->v_hadamard != 1)
+    return fail(RA_ERR_INVALID_ARG, "v_hadamard %d is not 0 or 1", o->v_hadamard);
   return RA_OK;
 }
 
@@ -243,6 +245,7 @@ ra::AttnArgs attn_args(ra_plan p, uint8_t* ws, void* o) {
   a.alpha_g = p->alpha_g;
   a.alpha = p->alpha;
   a.p_mode = p->opts.p_mode;
+  a.v_hadamard = p->opts.v_hadamard;
   return a;
 }
 
@@ -260,6 +263,7 @@ ra_status ra_opts_default(ra_opts* o) {
   o->rope_theta = 10000.0;
   o->softmax_scale = 0.0;
   o->p_mode = 0;
+  o->v_hadamard = 0;
   return ok();
 }
 
@@ -352,7 +356,7 @@ ra_status ra_attn_prologue(ra_plan p, const void* q, const void* k, const void* 
     va.N = p->lay.N;
     va.H = p->shape.heads;
     va.chunk = 512;
-    ra::launch_int4_prologue(qa, va, vq, D, p->opts.rot, in_bf16, stream);
+    ra::launch_int4_prologue(qa, va, vq, D, p->opts.rot, in_bf16, p->opts.v_hadamard != 0, stream);
   } else {
     ra::launch_bf16_prologue(qa, vq, D, in_bf16, stream);
   }

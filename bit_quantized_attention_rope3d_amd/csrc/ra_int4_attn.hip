@@ -431,6 +431,55 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
   }
 }
 
+// Output side of the V-side Hadamard: o <- o H, H = Walsh-Hadamard / sqrt(D),
+// over the 2 D/2 values of a query held by lanes l and l ^ 32 in O^T
+// accumulator order (channel dt*32 + 8g + 4hf + e in register 4g + e of
+// tile dt).  Butterflies over channel bits 0-1 (e), 2 (hf, across the two
+// lanes), 3-4 (g) and 5.. (dt), then x 1/sqrt(D).  Part of the float path.
+template <int D>
+__device__ __forceinline__ void fwht_out(v16f (&acc)[Cfg<D>::DT]) {
+  constexpr int DT = Cfg<D>::DT;
+  auto bfly_r = [&](int bit) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (!(r & bit)) {
+          const float lo = acc[dt][r], hi = acc[dt][r + bit];
+          acc[dt][r] = lo + hi;
+          acc[dt][r + bit] = lo - hi;
+        }
+  };
+  bfly_r(1);
+  bfly_r(2);
+  const bool upper = (threadIdx.x & 32) != 0;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float other = __shfl_xor(acc[dt][r], 32, 64);
+      acc[dt][r] = upper ? other - acc[dt][r] : acc[dt][r] + other;
+    }
+  bfly_r(4);
+  bfly_r(8);
+#pragma unroll
+  for (int bit = 1; bit < DT; bit <<= 1)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      if (!(dt & bit))
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float lo = acc[dt][r], hi = acc[dt + bit][r];
+          acc[dt][r] = lo + hi;
+          acc[dt + bit][r] = lo - hi;
+        }
+  const float sc = D == 128 ? 0.088388347648318440550f : 0.125f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] *= sc;
+}
+
 template <int D>
 __device__ __forceinline__ void state_init(State<D>& st) {
 #pragma unroll
@@ -442,7 +491,7 @@ __device__ __forceinline__ void state_init(State<D>& st) {
   st.U = 0u;
 }
 
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, bool VH>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * (C::KT + C::VT) + kPTabBytes];
@@ -556,11 +605,23 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     pv_step<D>(vst(t), p, st.acc);
   }
 
-  // o = A s_v / L: the 1/15 of the dequantized P cancels against the
-  // quantized row sum.
+  // o = A s_v / L: the scale of the dequantized P cancels against the
+  // quantized row sum.  With the V-side Hadamard the V codes are of V H, and
+  // the row is multiplied by H again.
   const float lw = st.L + (float)st.U;
   const float lt = xhalf_sum_f(lw);
   const float inv = 1.0f / lt;
+  if (VH) {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const v4f sv = *reinterpret_cast<const v4f*>(a.s_v + (size_t)bh * D + dt * 32 + 8 * g + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.acc[dt][4 * g + e] = st.acc[dt][4 * g + e] * sv[e] * inv;
+      }
+    fwht_out<D>(st.acc);
+  }
   const int q = q0 + ln;
   if (q < a.N) {
     const int b = bh / a.H, h = bh % a.H;
@@ -570,11 +631,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = dt * 32 + 8 * g + 4 * hf;
-        const v4f sv = *reinterpret_cast<const v4f*>(a.s_v + (size_t)bh * D + d);
         float o[4];
+        if (VH) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = st.acc[dt][4 * g + e] * sv[e] * inv;
+          for (int e = 0; e < 4; ++e) o[e] = st.acc[dt][4 * g + e];
+        } else {
+          const v4f sv = *reinterpret_cast<const v4f*>(a.s_v + (size_t)bh * D + d);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = st.acc[dt][4 * g + e] * sv[e] * inv;
+        }
         if (OUT_BF16) {
           uint16_t* op = static_cast<uint16_t*>(a.out) + obase + d;
           *reinterpret_cast<uint2*>(op) =
@@ -645,12 +710,24 @@ __global__ void k_copy1(const uint8_t* __restrict__ src, uint8_t* __restrict__ d
 
 void launch_int4_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st) {
   const unsigned nwg = (unsigned)(B * a.H * ((a.N + kQTile - 1) / kQTile));
+  const dim3 blk(64 * kWaves);
+  const bool vh = a.v_hadamard != 0;
   if (D == 128) {
-    if (out_bf16) k_int4_attn<128, true><<<nwg, 64 * kWaves, 0, st>>>(a);
-    else k_int4_attn<128, false><<<nwg, 64 * kWaves, 0, st>>>(a);
+    if (vh) {
+      if (out_bf16) k_int4_attn<128, true, true><<<nwg, blk, 0, st>>>(a);
+      else k_int4_attn<128, false, true><<<nwg, blk, 0, st>>>(a);
+    } else {
+      if (out_bf16) k_int4_attn<128, true, false><<<nwg, blk, 0, st>>>(a);
+      else k_int4_attn<128, false, false><<<nwg, blk, 0, st>>>(a);
+    }
   } else {
-    if (out_bf16) k_int4_attn<64, true><<<nwg, 64 * kWaves, 0, st>>>(a);
-    else k_int4_attn<64, false><<<nwg, 64 * kWaves, 0, st>>>(a);
+    if (vh) {
+      if (out_bf16) k_int4_attn<64, true, true><<<nwg, blk, 0, st>>>(a);
+      else k_int4_attn<64, false, true><<<nwg, blk, 0, st>>>(a);
+    } else {
+      if (out_bf16) k_int4_attn<64, true, false><<<nwg, blk, 0, st>>>(a);
+      else k_int4_attn<64, false, false><<<nwg, blk, 0, st>>>(a);
+    }
   }
 }
 

@@ -44,6 +44,7 @@ struct AttnArgs {
   float alpha_g;      // f32(log2(e) * softmax_scale * kPGrid)   (int4 path)
   float alpha;        // f32(log2(e) * softmax_scale)            (bf16 path)
   int p_mode;         // 0: range-optimized P (u = round(15 p), code u - 8); 1: symmetric (u = code = round(7 p))
+  int v_hadamard;     // V codes are of V H (H = Walsh-Hadamard / sqrt D): the output is multiplied by H
 };
 
 struct TileDumpArgs {
@@ -55,7 +56,7 @@ struct TileDumpArgs {
 };
 
 void launch_int4_prologue(const QKPrologueArgs& qa, const VAmaxArgs& va, const VQuantArgs& vq,
-                          int D, int rot, bool in_bf16, hipStream_t st);
+                          int D, int rot, bool in_bf16, bool v_hadamard, hipStream_t st);
 void launch_bf16_prologue(const QKPrologueArgs& qa, const VQuantArgs& vq, int D, bool in_bf16,
                           hipStream_t st);
 void launch_int4_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);

@@ -276,7 +276,43 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
 // ---------------------------------------------------------------------------
 // V per-channel amax over a chunk of tokens, merged with atomicMax on the
 // float bit pattern (order-preserving for non-negative floats).
-template <bool BF16, int D>
+// V-side Hadamard (a standard Hadamard transform fused into V, RotateAttention
+// review, summary and reproducibility notes): the orthonormal Walsh-Hadamard
+// transform of a row of D values held VEC consecutive values per lane by
+// D/VEC consecutive lanes.  Butterfly stages h = 1, 2, ..., D/2 in that
+// order, each pair (i, i + h), bit h of i clear, becoming (x_i + x_{i+h},
+// x_i - x_{i+h}): stages below VEC inside the lane, the others with the lane
+// whose index differs in bit h / VEC; then one multiply by f32(1/sqrt(D)).
+// Every lane of a row's group must execute it.
+template <int VEC, int D>
+__device__ __forceinline__ void fwht_row(float (&x)[VEC]) {
+#pragma unroll
+  for (int h = 1; h < VEC; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+      if (!(i & h)) {
+        const float lo = x[i], hi = x[i + h];
+        x[i] = lo + hi;
+        x[i + h] = lo - hi;
+      }
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = VEC; h < D; h <<= 1) {
+    const int m = h / VEC;
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const float other = __shfl_xor(x[i], m, 64);
+      x[i] = upper ? other - x[i] : x[i] + other;
+    }
+  }
+  constexpr float sc = D == 128 ? 0.088388347648318440550f : 0.125f;   // f32(1/sqrt(D))
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) x[i] = x[i] * sc;
+}
+
+template <bool BF16, int D, bool VH>
 __global__ __launch_bounds__(256) void k_v_amax(VAmaxArgs a) {
   typedef typename InT<BF16>::T T;
   constexpr int VEC = 16 / sizeof(T);      // elements per 16-byte load
@@ -294,6 +330,7 @@ __global__ __launch_bounds__(256) void k_v_amax(VAmaxArgs a) {
   for (int n = n0 + ph; n < n1; n += PH) {
     float v[VEC];
     load_row_part<BF16>(a.v, (((size_t)b * a.N + n) * a.H + h) * D + cg * VEC, VEC, v);
+    if (VH) fwht_row<VEC, D>(v);       // the CG lanes of row n share n
 #pragma unroll
     for (int e = 0; e < VEC; ++e) m[e] = fmaxf(m[e], fabsf(v[e]));
   }
@@ -315,7 +352,7 @@ __global__ void k_zero_u32(uint32_t* p, size_t n) {
 // V quantization + transpose into the PV operand layout: one workgroup per
 // (64-key block, b*h); each thread writes (channel, 16-slot group) units of
 // 16 e4m3 bytes.
-template <bool BF16, int D>
+template <bool BF16, int D, bool VH>
 __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
   constexpr int PER = D / 4;
   __shared__ float tile[64][D + 1];
@@ -330,6 +367,7 @@ __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) tmp[e] = 0.0f;
   }
+  if (VH) fwht_row<PER, D>(tmp);       // lanes 4r .. 4r+3 hold row r (padded rows stay 0)
 #pragma unroll
   for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = tmp[e];
   __syncthreads();
@@ -435,7 +473,7 @@ __global__ __launch_bounds__(256) void k_v_bf16(VQuantArgs a) {
   } while (0)
 
 void launch_int4_prologue(const QKPrologueArgs& qa, const VAmaxArgs& va, const VQuantArgs& vq,
-                          int D, int rot, bool in_bf16, hipStream_t st) {
+                          int D, int rot, bool in_bf16, bool vh, hipStream_t st) {
   const int BH = qa.B * qa.H;
   {
     size_t n = (size_t)BH * D;
@@ -447,14 +485,24 @@ void launch_int4_prologue(const QKPrologueArgs& qa, const VAmaxArgs& va, const V
       if (rot == 0) k_rope_quant_qk<0, true, D><<<gq, 256, 0, st>>>(qa);
       else if (rot == 1) k_rope_quant_qk<1, true, D><<<gq, 256, 0, st>>>(qa);
       else k_rope_quant_qk<2, true, D><<<gq, 256, 0, st>>>(qa);
-      k_v_amax<true, D><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
-      k_v_quant<true, D><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+      if (vh) {
+        k_v_amax<true, D, true><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
+        k_v_quant<true, D, true><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+      } else {
+        k_v_amax<true, D, false><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
+        k_v_quant<true, D, false><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+      }
     } else {
       if (rot == 0) k_rope_quant_qk<0, false, D><<<gq, 256, 0, st>>>(qa);
       else if (rot == 1) k_rope_quant_qk<1, false, D><<<gq, 256, 0, st>>>(qa);
       else k_rope_quant_qk<2, false, D><<<gq, 256, 0, st>>>(qa);
-      k_v_amax<false, D><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
-      k_v_quant<false, D><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+      if (vh) {
+        k_v_amax<false, D, true><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
+        k_v_quant<false, D, true><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+      } else {
+        k_v_amax<false, D, false><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
+        k_v_quant<false, D, false><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
+      }
     }
   });
 }

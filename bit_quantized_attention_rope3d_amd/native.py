@@ -33,7 +33,7 @@ class RaShape(ctypes.Structure):
 class RaOpts(ctypes.Structure):
     _fields_ = [("rot", c_i32), ("prec", c_i32), ("in_dtype", c_i32), ("out_dtype", c_i32),
                 ("rope_theta", c_f64), ("softmax_scale", c_f64), ("p_mode", c_i32),
-                ("reserved", c_i32)]
+                ("v_hadamard", c_i32)]
 
 
 class RaSchedule(ctypes.Structure):
@@ -116,7 +116,7 @@ def make_shape(batch, heads, head_dim, grid, seg) -> RaShape:
 
 
 def make_opts(rot="half", prec="int4", in_dtype="bf16", out_dtype="f32", rope_theta=10000.0,
-              softmax_scale=0.0, p_mode=0) -> RaOpts:
+              softmax_scale=0.0, p_mode=0, v_hadamard=0) -> RaOpts:
     o = RaOpts()
     check(lib().ra_opts_default(ctypes.byref(o)), "ra_opts_default")
     o.rot = ROT[rot] if isinstance(rot, str) else int(rot)
@@ -126,4 +126,5 @@ def make_opts(rot="half", prec="int4", in_dtype="bf16", out_dtype="f32", rope_th
     o.rope_theta = float(rope_theta)
     o.softmax_scale = float(softmax_scale)
     o.p_mode = int(p_mode)
+    o.v_hadamard = int(v_hadamard)
     return o

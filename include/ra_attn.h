@@ -76,7 +76,15 @@ typedef struct {
  * (default; code = round(15 p) - 8, the full signed range [-8, 7]), 1 =
  * symmetric quantization, the baseline the pages improve on (code = round(7 p)
  * in [0, 7], half of the codes unused); other values return
- * RA_ERR_INVALID_ARG.  The bf16 path ignores it. */
+ * RA_ERR_INVALID_ARG.  The bf16 path ignores it.
+ * v_hadamard = 1 applies the V-side Hadamard of the pages (a standard
+ * Hadamard transform fused into V; RotateAttention review, summary): each V
+ * row is multiplied by H = H_D / sqrt(D) (Walsh-Hadamard, Sylvester order;
+ * binary32 butterflies h = 1, 2, ..., D/2, then x f32(1/sqrt(D))) before its
+ * per-channel INT4 quantization, and each output row by H again (H = H^-1),
+ * so o is still attention(Q, K, V).  The V codes and scales reported by
+ * ra_debug_prologue are then those of V H.  Default 0; values other than 0
+ * and 1 return RA_ERR_INVALID_ARG; the bf16 path ignores it. */
 typedef struct {
   int32_t rot;        /* ra_rot */
   int32_t prec;       /* ra_prec */
@@ -85,7 +93,7 @@ typedef struct {
   double rope_theta;
   double softmax_scale;
   int32_t p_mode;
-  int32_t reserved;
+  int32_t v_hadamard; /* 0 or 1, see above */
 } ra_opts;
 
 typedef struct ra_plan_s* ra_plan;

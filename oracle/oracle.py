@@ -25,7 +25,7 @@ BLOCK = 64
 __all__ = [
     "build", "lib", "ROT_NONE", "ROT_INTERLEAVED", "ROT_HALF", "ROT_NAMES",
     "BLOCK", "pgrid", "bf16_bits_to_f32", "as_f32", "rope_table", "rope_rotate",
-    "quant_qk", "quant_v", "prologue", "pmap_thresholds", "pmap", "P_SCALE", "P_ZERO",
+    "quant_qk", "quant_v", "fwht", "prologue", "pmap_thresholds", "pmap", "P_SCALE", "P_ZERO",
     "attention_rows", "attention_tile", "attention_full", "schedule_full_precision",
     "set_threads", "get_threads",
 ]
@@ -63,12 +63,13 @@ def lib():
             L.ora_pmap.argtypes = [P, ctypes.c_int64, P]
             L.ora_pmap_thresholds_p.argtypes = [i32, i32, P]
             L.ora_pmap_p.argtypes = [P, ctypes.c_int64, i32, P]
-            L.ora_attention_head.argtypes = [P, P, P, P, P, P, i32, i32, f64, i32,
+            L.ora_fwht_rows.argtypes = [P, ctypes.c_int64, i32]
+            L.ora_attention_head.argtypes = [P, P, P, P, P, P, i32, i32, f64, i32, i32,
                                              P, i32, P, P, i32, P, P, P, P]
             L.ora_schedule_full_precision.argtypes = [i32] * 8
             for name in ("ora_rope_table", "ora_rope_rotate", "ora_quant_qk",
                          "ora_quant_v", "ora_pmap_thresholds", "ora_pmap",
-                         "ora_pmap_thresholds_p", "ora_pmap_p",
+                         "ora_pmap_thresholds_p", "ora_pmap_p", "ora_fwht_rows",
                          "ora_attention_head", "ora_schedule_full_precision"):
                 getattr(L, name).restype = i32
             _lib = L
@@ -149,15 +150,25 @@ def quant_v(v):
     return codes, scales
 
 
-def prologue(q, k, v, grid, seg, theta=10000.0, rot=ROT_HALF):
-    """RoPE + rotation + INT4 quantization of Q/K, and INT4 quantization of V."""
+def fwht(x):
+    """Orthonormal Walsh-Hadamard transform of the last axis in binary32
+    (butterflies h = 1, 2, ..., then x f32(1/sqrt(D)))."""
+    x = np.array(as_f32(x), dtype=np.float32, copy=True, order="C")
+    D = x.shape[-1]
+    _check(lib().ora_fwht_rows(_p(x), x.size // D, D), "fwht_rows")
+    return x
+
+
+def prologue(q, k, v, grid, seg, theta=10000.0, rot=ROT_HALF, v_hadamard=False):
+    """RoPE + rotation + INT4 quantization of Q/K, and INT4 quantization of V
+    (of V H when v_hadamard)."""
     qr = rope_rotate(q, grid, seg, theta, rot)
     kr = rope_rotate(k, grid, seg, theta, rot)
     qc, sq = quant_qk(qr)
     del qr
     kc, sk = quant_qk(kr)
     del kr
-    vc, sv = quant_v(v)
+    vc, sv = quant_v(fwht(v) if v_hadamard else v)
     return dict(q_codes=qc, s_q=sq, k_codes=kc, s_k=sk, v_codes=vc, s_v=sv)
 
 
@@ -185,7 +196,7 @@ def _head(pro, b, h):
             np.ascontiguousarray(pro["v_codes"][b, h]), np.ascontiguousarray(pro["s_v"][b, h]))
 
 
-def attention_rows(pro, b, h, rows, softmax_scale=None, with_m=False, p_mode=0):
+def attention_rows(pro, b, h, rows, softmax_scale=None, with_m=False, p_mode=0, v_hadamard=False):
     """Oracle output rows (binary64) of head (b, h) for query indices `rows`."""
     qc, sq, kc, sk, vc, sv = _head(pro, b, h)
     N, D = qc.shape
@@ -194,7 +205,8 @@ def attention_rows(pro, b, h, rows, softmax_scale=None, with_m=False, p_mode=0):
     o = np.empty((rows.size, D), np.float64)
     m = np.empty(rows.size, np.float32)
     _check(lib().ora_attention_head(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), N, D,
-                                    scale, int(p_mode), _p(rows), rows.size, _p(o), _p(m), -1,
+                                    scale, int(p_mode), int(bool(v_hadamard)), _p(rows), rows.size,
+                                    _p(o), _p(m), -1,
                                     None, None, None, None), "attention_head")
     return (o, m) if with_m else o
 
@@ -216,20 +228,21 @@ def attention_tile(pro, b, h, q_blk, kv_blk, softmax_scale=None, p_mode=0):
     pv = np.zeros((n, D), np.int32)
     m_after = np.zeros(n, np.float32)
     _check(lib().ora_attention_head(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), N, D,
-                                    scale, int(p_mode), _p(rows), n, _p(o), None, int(kv_blk),
+                                    scale, int(p_mode), 0, _p(rows), n, _p(o), None, int(kv_blk),
                                     _p(s_int), _p(p_code), _p(pv), _p(m_after)),
            "attention_tile")
     return dict(s_int=s_int, p_code=p_code, pv_int=pv, m_after=m_after)
 
 
-def attention_full(pro, softmax_scale=None, p_mode=0):
+def attention_full(pro, softmax_scale=None, p_mode=0, v_hadamard=False):
     """Oracle output [B, N, H, D] (binary64) for every row of every head."""
     B, H, N, D = pro["q_codes"].shape
     out = np.empty((B, N, H, D), np.float64)
     rows = np.arange(N, dtype=np.int32)
     for b in range(B):
         for h in range(H):
-            out[b, :, h, :] = attention_rows(pro, b, h, rows, softmax_scale, p_mode=p_mode)
+            out[b, :, h, :] = attention_rows(pro, b, h, rows, softmax_scale, p_mode=p_mode,
+                                             v_hadamard=v_hadamard)
     return out
 
 

@@ -237,6 +237,49 @@ int ora_quant_v(const float *v, int B, int N, int H, int D,
 }
 
 /* ------------------------------------------------------------------------ */
+/* V-side Hadamard ([RA] summary and reproducibility notes: a standard
+ * Hadamard transform fused offline into V).  Reading: each V row is
+ * multiplied by the orthonormal Walsh-Hadamard matrix H = H_D / sqrt(D)
+ * (Sylvester order) before the per-channel quantization, and the attention
+ * output row by the same matrix (symmetric and its own inverse), so the
+ * operator still returns attention(Q, K, V); in a model the second product
+ * would be folded into the output projection.  Binary32, in this order:
+ * butterfly stages h = 1, 2, 4, ..., D/2, each pair (i, i + h) with bit h of
+ * i clear becoming (x_i + x_{i+h}, x_i - x_{i+h}); then one multiply of every
+ * element by f32(1/sqrt(D)).                                               */
+int ora_fwht_rows(float *x, int64_t rows, int D)
+{
+    if (D < 1 || (D & (D - 1))) return -1;
+    const float sc = (float)(1.0 / sqrt((double)D));
+    for (int64_t r = 0; r < rows; ++r) {
+        float *v = x + r * D;
+        for (int h = 1; h < D; h <<= 1)
+            for (int i = 0; i < D; ++i)
+                if (!(i & h)) {
+                    float a = v[i], b = v[i + h];
+                    v[i] = a + b;
+                    v[i + h] = a - b;
+                }
+        for (int i = 0; i < D; ++i) v[i] = v[i] * sc;
+    }
+    return 0;
+}
+
+/* The same transform in binary64 (the output side of the float path). */
+static void fwht_f64(double *v, int D)
+{
+    for (int h = 1; h < D; h <<= 1)
+        for (int i = 0; i < D; ++i)
+            if (!(i & h)) {
+                double a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    const double sc = 1.0 / sqrt((double)D);
+    for (int i = 0; i < D; ++i) v[i] *= sc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Range-optimized P map ([RA] Sec. 4.2: fixed scale 15, zero-point -8, so
  * p in [0,1] covers the whole signed INT4 range [-8, 7]).
  * code = round(15 p) - 8, p = 2^(x/G) with x the integer exponent on the grid
@@ -312,7 +355,8 @@ static float mul_round_up(int32_t s, float c)
  *   sums       U = sum_j u_j;  num_c = sum_j u_j vhat_jc;
  *              PV_c = sum_j code_j vhat_jc = num_c - 8 sum_j vhat_jc
  *   float path (binary64):  beta = 2^((m_old - m)/G),
- *              A = A beta + num,  L = L beta + U,  o = A s_v / L.
+ *              A = A beta + num,  L = L beta + U,  o = A s_v / L,
+ *              times H when the V codes are of V H (v_hadamard).
  * The dequantized P is u/15 (u/7), so the scale cancels in A/L: the row is
  * normalised by the sum of its quantized probabilities.
  *
@@ -325,7 +369,7 @@ static float mul_round_up(int32_t s, float c)
 int ora_attention_head(const int8_t *qc, const float *sq,
                        const int8_t *kc, const float *sk,
                        const int8_t *vc, const float *sv,
-                       int N, int D, double softmax_scale, int p_mode,
+                       int N, int D, double softmax_scale, int p_mode, int v_hadamard,
                        const int32_t *rows, int nrows, double *o, float *m_out,
                        int dbg_kb, int32_t *s_int, int8_t *p_code,
                        int32_t *pv_int, float *m_after)
@@ -398,6 +442,7 @@ int ora_attention_head(const int8_t *qc, const float *sq,
         }
         for (int c2 = 0; c2 < D; ++c2)
             o[(size_t)r * D + c2] = A[c2] * (double)sv[c2] / L;
+        if (v_hadamard) fwht_f64(o + (size_t)r * D, D);   /* back from the rotated V basis */
         if (m_out) m_out[r] = m;
     }
     return 0;

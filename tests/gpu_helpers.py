@@ -19,10 +19,11 @@ def dev(x: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
 
 
-def plan_for(w, prec="int4", out_dtype="f32", p_mode=0):
+def plan_for(w, prec="int4", out_dtype="f32", p_mode=0, v_hadamard=0):
     from bit_quantized_attention_rope3d_amd.api import Plan
     return Plan(w.batch, w.heads, w.head_dim, w.grid, w.seg, rot=w.rot, prec=prec,
-                in_dtype=w.dtype, out_dtype=out_dtype, rope_theta=w.theta, p_mode=p_mode)
+                in_dtype=w.dtype, out_dtype=out_dtype, rope_theta=w.theta, p_mode=p_mode,
+                v_hadamard=v_hadamard)
 
 
 def cosine(a, b):

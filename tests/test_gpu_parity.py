@@ -243,3 +243,36 @@ def test_symmetric_mode_matches_oracle(ora, case):
     say("symmetric %s: max|gpu-oracle| %.2e cos %.7f | vs fp64: symmetric mean %.3e, range-optimized mean %.3e"
         % (case, err, cos, np.abs(o - ref).mean(), np.abs(o0 - ref).mean()))
     assert err <= 2e-3 and cos >= 0.999
+
+
+# ---- V-side Hadamard (v_hadamard = 1) ---------------------------------------
+
+@pytest.mark.parametrize("case", ["tiny", "small", "small_d64", "medium", "batch2"])
+def test_v_hadamard_matches_oracle(ora, case):
+    """V rows times H = Walsh-Hadamard / sqrt(D) before the per-channel INT4
+    quantization (the summary's offline-fused Hadamard on V), output rows
+    times H again: V codes and scales bit-exact, tiles bit-exact, output within
+    tolerance of the oracle's float path."""
+    w = CASES[case]
+    q, k, v, _ = inputs.generate(w)
+    pro = ora.prologue(q, k, v, w.grid, w.seg, w.theta, w.rot_id, v_hadamard=True)
+    p = plan_for(w, v_hadamard=1)
+    got = p.debug_prologue(dev(q), dev(k), dev(v))
+    assert np.array_equal(got["v_codes"], pro["v_codes"]), case
+    assert np.array_equal(got["s_v"].view(np.uint32), pro["s_v"].view(np.uint32)), case
+    ws = p.workspace()
+    p.prologue(dev(q), dev(k), dev(v), ws)
+    nb = (w.tokens + 63) // 64
+    for qb, kb in sorted({(0, 0), (nb - 1, nb - 1), (0, nb - 1)}):
+        g = p.debug_tile(ws, 0, 0, qb, kb)
+        t = ora.attention_tile({kk: vv[0:1] for kk, vv in pro.items()}, 0, 0, qb, kb)
+        n = t["s_int"].shape[0]
+        assert np.array_equal(g["pv_int"][:n], t["pv_int"]), (case, qb, kb)
+    o = p.forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    want = ora.attention_full(pro, v_hadamard=True)
+    err, cos = np.abs(o - want).max(), cosine(o, want)
+    ref = ref_fp64.reference_output(ora.as_f32(q), ora.as_f32(k), ora.as_f32(v), w.grid, w.seg, w.theta)
+    o0 = plan_for(w).forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    say("v_hadamard %s: max|gpu-oracle| %.2e cos %.7f | vs fp64 mean: with H %.3e, without %.3e"
+        % (case, err, cos, np.abs(o - ref).mean(), np.abs(o0 - ref).mean()))
+    assert err <= 2e-3 and cos >= 0.999
