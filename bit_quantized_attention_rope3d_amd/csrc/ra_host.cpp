@@ -76,7 +76,7 @@ ra_status validate(const ra_shape* s, const ra_opts* o) {
   if (s->seg[0] + s->seg[1] + s->seg[2] != s->head_dim)
     return fail(RA_ERR_SEGMENTS, "segments %d+%d+%d do not sum to head_dim %d", s->seg[0], s->seg[1],
                 s->seg[2], s->head_dim);
-  if (o->rot < RA_ROT_NONE || o->rot > RA_ROT_HALF)
+  if (o->rot < RA_ROT_NONE || o->rot > RA_ROT_FULL)
     return fail(RA_ERR_INVALID_ARG, "rot %d is not a ra_rot", o->rot);
   if (o->prec != RA_PREC_INT4 && o->prec != RA_PREC_BF16)
     return fail(RA_ERR_INVALID_ARG, "prec %d is not a ra_prec", o->prec);

@@ -170,12 +170,49 @@ __device__ __forceinline__ void load_group_codes(const uint8_t* p, uint32_t (&cw
   cw[4] = b.x; cw[5] = b.y; cw[6] = b.z; cw[7] = b.w;
 }
 
+// Orthonormal Walsh-Hadamard transform (the full rotation of Q/K, and the
+// V-side Hadamard of the RotateAttention review's summary) of a row of D
+// values held VEC consecutive values per lane by
+// D/VEC consecutive lanes.  Butterfly stages h = 1, 2, ..., D/2 in that
+// order, each pair (i, i + h), bit h of i clear, becoming (x_i + x_{i+h},
+// x_i - x_{i+h}): stages below VEC inside the lane, the others with the lane
+// whose index differs in bit h / VEC; then one multiply by f32(1/sqrt(D)).
+// Every lane of a row's group must execute it.
+template <int VEC, int D>
+__device__ __forceinline__ void fwht_row(float (&x)[VEC]) {
+#pragma unroll
+  for (int h = 1; h < VEC; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+      if (!(i & h)) {
+        const float lo = x[i], hi = x[i + h];
+        x[i] = lo + hi;
+        x[i + h] = lo - hi;
+      }
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = VEC; h < D; h <<= 1) {
+    const int m = h / VEC;
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const float other = __shfl_xor(x[i], m, 64);
+      x[i] = upper ? other - x[i] : x[i] + other;
+    }
+  }
+  constexpr float sc = D == 128 ? 0.088388347648318440550f : 0.125f;   // f32(1/sqrt(D))
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) x[i] = x[i] * sc;
+}
+
 // ---------------------------------------------------------------------------
 // Q/K: one workgroup per (64-token block, b*h, tensor); each of the 4 waves
 // takes 16 rows of the block (PairLane layout).  RoPE per pair, then (ROT ==
 // 2) the Half rotation u' = (u + w) r, w' = (u - w) r on channels
 // (i, i + L/2) of each segment through a per-wave LDS row, r = f32(1/sqrt 2);
-// ROT == 1 (Interleaved) is already merged into the tables as +pi/4.  The
+// ROT == 1 (Interleaved) is already merged into the tables as +pi/4; ROT ==
+// 3 (Full) multiplies the whole RoPE'd row by the Walsh-Hadamard matrix.  The
 // rotated values stay in registers for the block amax, then become fp6 e2m3
 // codes, one per byte in an LDS tile, which the workgroup packs into the
 // 64-token fp6 tile and writes with coalesced 16-byte stores.
@@ -236,6 +273,12 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
       y[it][1] = __builtin_fmaf(y[it][1], sgn[1], o1) * r;
     }
   }
+  // Full rotation: the whole RoPE'd row times the Walsh-Hadamard matrix; the
+  // PAIRS lanes of a row hold it two values each.
+  if (ROT == 3) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) fwht_row<2, D>(y[it]);
+  }
   float mx = 0.0f;
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) mx = fmaxf(mx, fmaxf(fabsf(y[it][0]), fabsf(y[it][1])));
@@ -276,42 +319,6 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
 // ---------------------------------------------------------------------------
 // V per-channel amax over a chunk of tokens, merged with atomicMax on the
 // float bit pattern (order-preserving for non-negative floats).
-// V-side Hadamard (a standard Hadamard transform fused into V, RotateAttention
-// review, summary and reproducibility notes): the orthonormal Walsh-Hadamard
-// transform of a row of D values held VEC consecutive values per lane by
-// D/VEC consecutive lanes.  Butterfly stages h = 1, 2, ..., D/2 in that
-// order, each pair (i, i + h), bit h of i clear, becoming (x_i + x_{i+h},
-// x_i - x_{i+h}): stages below VEC inside the lane, the others with the lane
-// whose index differs in bit h / VEC; then one multiply by f32(1/sqrt(D)).
-// Every lane of a row's group must execute it.
-template <int VEC, int D>
-__device__ __forceinline__ void fwht_row(float (&x)[VEC]) {
-#pragma unroll
-  for (int h = 1; h < VEC; h <<= 1)
-#pragma unroll
-    for (int i = 0; i < VEC; ++i)
-      if (!(i & h)) {
-        const float lo = x[i], hi = x[i + h];
-        x[i] = lo + hi;
-        x[i + h] = lo - hi;
-      }
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int h = VEC; h < D; h <<= 1) {
-    const int m = h / VEC;
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const float other = __shfl_xor(x[i], m, 64);
-      x[i] = upper ? other - x[i] : x[i] + other;
-    }
-  }
-  constexpr float sc = D == 128 ? 0.088388347648318440550f : 0.125f;   // f32(1/sqrt(D))
-  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) x[i] = x[i] * sc;
-}
-
 template <bool BF16, int D, bool VH>
 __global__ __launch_bounds__(256) void k_v_amax(VAmaxArgs a) {
   typedef typename InT<BF16>::T T;
@@ -484,7 +491,8 @@ void launch_int4_prologue(const QKPrologueArgs& qa, const VAmaxArgs& va, const V
     if (in_bf16) {
       if (rot == 0) k_rope_quant_qk<0, true, D><<<gq, 256, 0, st>>>(qa);
       else if (rot == 1) k_rope_quant_qk<1, true, D><<<gq, 256, 0, st>>>(qa);
-      else k_rope_quant_qk<2, true, D><<<gq, 256, 0, st>>>(qa);
+      else if (rot == 2) k_rope_quant_qk<2, true, D><<<gq, 256, 0, st>>>(qa);
+      else k_rope_quant_qk<3, true, D><<<gq, 256, 0, st>>>(qa);
       if (vh) {
         k_v_amax<true, D, true><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
         k_v_quant<true, D, true><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);
@@ -495,7 +503,8 @@ void launch_int4_prologue(const QKPrologueArgs& qa, const VAmaxArgs& va, const V
     } else {
       if (rot == 0) k_rope_quant_qk<0, false, D><<<gq, 256, 0, st>>>(qa);
       else if (rot == 1) k_rope_quant_qk<1, false, D><<<gq, 256, 0, st>>>(qa);
-      else k_rope_quant_qk<2, false, D><<<gq, 256, 0, st>>>(qa);
+      else if (rot == 2) k_rope_quant_qk<2, false, D><<<gq, 256, 0, st>>>(qa);
+      else k_rope_quant_qk<3, false, D><<<gq, 256, 0, st>>>(qa);
       if (vh) {
         k_v_amax<false, D, true><<<dim3((va.N + va.chunk - 1) / va.chunk, BH), 256, 0, st>>>(va);
         k_v_quant<false, D, true><<<dim3(vq.nkb, BH), 256, 0, st>>>(vq);

@@ -16,7 +16,7 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-ROT = {"none": 0, "interleaved": 1, "half": 2}
+ROT = {"none": 0, "interleaved": 1, "half": 2, "full": 3}
 
 
 @dataclass(frozen=True)
@@ -27,7 +27,7 @@ class Workload:
     head_dim: int
     grid: tuple            # (F, H, W) token grid, w fastest
     seg: tuple             # (frame, height, width) head-dim split
-    rot: str = "half"      # none | interleaved | half
+    rot: str = "half"      # none | interleaved | half | full
     dtype: str = "bf16"    # input dtype: bf16 | f32
     theta: float = 10000.0
     seed: int = 0

@@ -19,7 +19,7 @@ c_i32, c_i64, c_f64, c_size, c_void = (ctypes.c_int32, ctypes.c_int64, ctypes.c_
 RA_OK = 0
 STATUS = ["RA_OK", "RA_ERR_INVALID_ARG", "RA_ERR_SHAPE", "RA_ERR_SEGMENTS", "RA_ERR_DTYPE",
           "RA_ERR_ALIGNMENT", "RA_ERR_WORKSPACE", "RA_ERR_UNSUPPORTED", "RA_ERR_OOM", "RA_ERR_HIP"]
-ROT = {"none": 0, "interleaved": 1, "half": 2}
+ROT = {"none": 0, "interleaved": 1, "half": 2, "full": 3}
 PREC = {"int4": 0, "bf16": 1}
 DT = {"f32": 0, "bf16": 1}
 

@@ -58,7 +58,14 @@ typedef enum {
   RA_ERR_HIP = 9            /* a HIP runtime call or kernel launch failed */
 } ra_status;
 
-typedef enum { RA_ROT_NONE = 0, RA_ROT_INTERLEAVED = 1, RA_ROT_HALF = 2 } ra_rot;
+/* Rotation of Q and K after RoPE (RotateAttention review, Sec. 4.1 / Fig. 3
+ * and Figs. 4-6): NONE; INTERLEAVED, R(pi/4) on each RoPE pair, merged into
+ * the RoPE angles; HALF, H2 on (x_i, x_{i+L/2}) within each segment; FULL,
+ * the dense comparator of Figs. 4-6 that rotates all D dimensions at once,
+ * here the orthonormal Walsh-Hadamard matrix (binary32 butterflies h = 1, 2,
+ * ..., D/2, then x f32(1/sqrt(D))) applied to the whole RoPE'd head row.
+ * The bf16 path applies none of them. */
+typedef enum { RA_ROT_NONE = 0, RA_ROT_INTERLEAVED = 1, RA_ROT_HALF = 2, RA_ROT_FULL = 3 } ra_rot;
 typedef enum { RA_PREC_INT4 = 0, RA_PREC_BF16 = 1 } ra_prec;
 typedef enum { RA_DT_F32 = 0, RA_DT_BF16 = 1 } ra_dtype;
 

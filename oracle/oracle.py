@@ -18,12 +18,12 @@ _LIB_PATH = os.path.join(_HERE, "libra_oracle.so")
 _lib = None
 _lock = threading.Lock()
 
-ROT_NONE, ROT_INTERLEAVED, ROT_HALF = 0, 1, 2
-ROT_NAMES = {"none": ROT_NONE, "interleaved": ROT_INTERLEAVED, "half": ROT_HALF}
+ROT_NONE, ROT_INTERLEAVED, ROT_HALF, ROT_FULL = 0, 1, 2, 3
+ROT_NAMES = {"none": ROT_NONE, "interleaved": ROT_INTERLEAVED, "half": ROT_HALF, "full": ROT_FULL}
 BLOCK = 64
 
 __all__ = [
-    "build", "lib", "ROT_NONE", "ROT_INTERLEAVED", "ROT_HALF", "ROT_NAMES",
+    "build", "lib", "ROT_NONE", "ROT_INTERLEAVED", "ROT_HALF", "ROT_FULL", "ROT_NAMES",
     "BLOCK", "pgrid", "bf16_bits_to_f32", "as_f32", "rope_table", "rope_rotate",
     "quant_qk", "quant_v", "fwht", "prologue", "pmap_thresholds", "pmap", "P_SCALE", "P_ZERO",
     "attention_rows", "attention_tile", "attention_full", "schedule_full_precision",

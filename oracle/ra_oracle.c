@@ -32,7 +32,7 @@
 #include <string.h>
 #include <omp.h>
 
-enum { ORA_ROT_NONE = 0, ORA_ROT_INTERLEAVED = 1, ORA_ROT_HALF = 2 };
+enum { ORA_ROT_NONE = 0, ORA_ROT_INTERLEAVED = 1, ORA_ROT_HALF = 2, ORA_ROT_FULL = 3 };
 enum { ORA_BLOCK = 64 };      /* tokens per Q/K scale block and per key step */
 enum { ORA_CODE_MAX = 7 };    /* symmetric INT4 codes in [-7, 7] */
 enum { ORA_MAX_D = 256 };
@@ -83,13 +83,35 @@ int ora_rope_table(int npos, int L, double theta, int rot, float *cs, float *sn)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Orthonormal Walsh-Hadamard transform of one row v[D] (D a power of two) in
+ * binary32, in this order: butterfly stages h = 1, 2, 4, ..., D/2, each pair
+ * (i, i + h) with bit h of i clear becoming (v_i + v_{i+h}, v_i - v_{i+h});
+ * then one multiply of every element by f32(1/sqrt(D)).  Used for the full
+ * rotation of Q/K and the V-side Hadamard.                                  */
+static void fwht_f32(float *v, int D)
+{
+    const float sc = (float)(1.0 / sqrt((double)D));
+    for (int h = 1; h < D; h <<= 1)
+        for (int i = 0; i < D; ++i)
+            if (!(i & h)) {
+                float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    for (int i = 0; i < D; ++i) v[i] = v[i] * sc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* RoPE + RoPE-aware rotation of one token row x[D] -> y[D] (binary32).
  * Pair rotation (a, b) -> (a c - b s, a s + b c), each product rounded, then
  * the sum/difference rounded.
  * Half rotation ([RA] Sec. 4.1 / Fig. 3: each dim paired with its counterpart
  * in the other half of the segment; block H2 = (1/sqrt2)[[1,1],[1,-1]] by the
  * free-parameter ledger) is applied after RoPE:
- *   u' = (u + w) r,  w' = (u - w) r,  r = binary32(1/sqrt2).                 */
+ *   u' = (u + w) r,  w' = (u - w) r,  r = binary32(1/sqrt2).
+ * Full rotation (the dense comparator of [RA] Figs. 4-6, which rotates all D
+ * dimensions of the head at once; reading: the orthonormal Walsh-Hadamard
+ * matrix) is applied to the whole RoPE'd row: y = fwht(RoPE(x)).             */
 static void rotate_row(const float *x, float *y, int D, const int *seg,
                        const int *pos, float *const *cs, float *const *sn,
                        int rot)
@@ -120,16 +142,18 @@ static void rotate_row(const float *x, float *y, int D, const int *seg,
         }
         off += L;
     }
+    if (rot == ORA_ROT_FULL) fwht_f32(y, D);
 }
 
 /* x, y: [B, N, H, D] binary32.  Token n -> (f, h, w) in row-major order with
- * w fastest (N = F*Hh*W).  rot: 0 none, 1 interleaved (merged), 2 half. */
+ * w fastest (N = F*Hh*W).  rot: 0 none, 1 interleaved (merged), 2 half,
+ * 3 full (D must be a power of two). */
 int ora_rope_rotate(const float *x, float *y, int B, int H, int D,
                     int F, int Hh, int W, const int *seg, double theta, int rot)
 {
     if (D > ORA_MAX_D || seg[0] + seg[1] + seg[2] != D) return -1;
     for (int s = 0; s < 3; ++s) if (seg[s] < 2 || (seg[s] & 1)) return -1;
-    if (rot < 0 || rot > 2) return -1;
+    if (rot < 0 || rot > 3 || (rot == ORA_ROT_FULL && (D & (D - 1)))) return -1;
     int dims[3] = {F, Hh, W};
     float *cs[3], *sn[3];
     for (int s = 0; s < 3; ++s) {
@@ -250,18 +274,7 @@ int ora_quant_v(const float *v, int B, int N, int H, int D,
 int ora_fwht_rows(float *x, int64_t rows, int D)
 {
     if (D < 1 || (D & (D - 1))) return -1;
-    const float sc = (float)(1.0 / sqrt((double)D));
-    for (int64_t r = 0; r < rows; ++r) {
-        float *v = x + r * D;
-        for (int h = 1; h < D; h <<= 1)
-            for (int i = 0; i < D; ++i)
-                if (!(i & h)) {
-                    float a = v[i], b = v[i + h];
-                    v[i] = a + b;
-                    v[i + h] = a - b;
-                }
-        for (int i = 0; i < D; ++i) v[i] = v[i] * sc;
-    }
+    for (int64_t r = 0; r < rows; ++r) fwht_f32(x + r * D, D);
     return 0;
 }
 

@@ -74,7 +74,8 @@ def test_shape_validation(L, kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(rot=3), "RA_ERR_INVALID_ARG"),
+    (dict(rot=4), "RA_ERR_INVALID_ARG"),
+    (dict(v_hadamard=2), "RA_ERR_INVALID_ARG"),
     (dict(prec=2), "RA_ERR_INVALID_ARG"),
     (dict(in_dtype=5), "RA_ERR_DTYPE"),
     (dict(out_dtype=-1), "RA_ERR_DTYPE"),

@@ -276,3 +276,27 @@ def test_v_hadamard_matches_oracle(ora, case):
     say("v_hadamard %s: max|gpu-oracle| %.2e cos %.7f | vs fp64 mean: with H %.3e, without %.3e"
         % (case, err, cos, np.abs(o - ref).mean(), np.abs(o0 - ref).mean()))
     assert err <= 2e-3 and cos >= 0.999
+
+
+# ---- full rotation (rot = full) ---------------------------------------------
+
+@pytest.mark.parametrize("case", ["tiny", "small", "small_d64", "medium"])
+def test_full_rotation_matches_oracle(ora, case):
+    """rot = full: the RoPE'd Q/K rows times the Walsh-Hadamard matrix (the
+    dense comparator of Figs. 4-6) in the prologue; codes and scales
+    bit-exact, output within tolerance of the oracle."""
+    w = CASES[case].with_(name=case + "_full", rot="full")
+    q, k, v, pro = _prep(ora, w)
+    p = plan_for(w)
+    got = p.debug_prologue(dev(q), dev(k), dev(v))
+    for key in ("q_codes", "k_codes"):
+        assert np.array_equal(got[key], pro[key]), (case, key)
+    for key in ("s_q", "s_k"):
+        assert np.array_equal(got[key].view(np.uint32), pro[key].view(np.uint32)), (case, key)
+    o = p.forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    want = ora.attention_full(pro)
+    err, cos = np.abs(o - want).max(), cosine(o, want)
+    ref = ref_fp64.reference_output(ora.as_f32(q), ora.as_f32(k), ora.as_f32(v), w.grid, w.seg, w.theta)
+    say("full rotation %s: max|gpu-oracle| %.2e cos %.7f | vs fp64 mean %.3e"
+        % (case, err, cos, np.abs(o - ref).mean()))
+    assert err <= 2e-3 and cos >= 0.999

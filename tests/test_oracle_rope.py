@@ -140,3 +140,34 @@ def test_half_rotation_spreads_a_segment_outlier():
     x[:, c] = 20.0 * np.sign(rng.standard_normal(512))
     y = x @ ref.rotation_matrix(SEG, 2).T
     assert np.abs(y).max() < np.abs(x).max() / np.sqrt(2) * 1.05
+
+
+# ---- full rotation (rot = 3) -----------------------------------------------
+# Figs. 4-6 compare against a full rotation of all D dimensions; reading: the
+# orthonormal Walsh-Hadamard matrix applied to the RoPE'd head row.
+
+def test_full_rotation_is_hadamard_times_rope(ora):
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(21)
+    grid, seg = (2, 3, 5), (24, 20, 20)
+    x = rng.standard_normal((1, 30, 2, 64)).astype(np.float32)
+    y0 = ora.rope_rotate(x, grid, seg, 10000.0, 0).astype(np.float64)
+    y3 = ora.rope_rotate(x, grid, seg, 10000.0, 3).astype(np.float64)
+    want = y0 @ (hadamard(64) / np.sqrt(64))
+    assert np.abs(y3 - want).max() <= 1e-5 * np.abs(y0).max()
+    # orthogonal: norms and all scores q.k are kept (fp32 rounding aside)
+    assert np.allclose(np.linalg.norm(y3, axis=-1), np.linalg.norm(y0, axis=-1), rtol=1e-5)
+    s0 = np.einsum("bnhd,bmhd->bhnm", y0, y0)
+    s3 = np.einsum("bnhd,bmhd->bhnm", y3, y3)
+    assert np.abs(s3 - s0).max() <= 1e-4 * np.abs(s0).max()
+
+
+def test_full_rotation_spreads_any_channel_outlier(ora):
+    """One large channel anywhere in the row ends up as equal magnitudes in
+    every channel (unlike Half, which only pairs inside its segment)."""
+    x = np.zeros((1, 1, 1, 128), np.float32)
+    x[0, 0, 0, 77] = 100.0          # position 0: RoPE leaves the row as is
+    y = ora.rope_rotate(x, (1, 1, 1), (44, 42, 42), 10000.0, 3)
+    assert np.allclose(np.abs(y), 100.0 / np.sqrt(128), rtol=1e-6)
+    yh = ora.rope_rotate(x, (1, 1, 1), (44, 42, 42), 10000.0, 2)
+    assert np.count_nonzero(yh) == 2
