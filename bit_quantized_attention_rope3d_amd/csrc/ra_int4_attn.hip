@@ -17,26 +17,28 @@
 //     bytes for D = 128) are copied from global memory straight into LDS by
 //     buffer loads with the LDS-direct bit (16 bytes per lane, no VGPRs, no
 //     VALU); the XOR swizzle of the V rows is applied through the source
-//     addresses, the K tile needs none.  Two stages, issued one step ahead,
-//     one barrier per step.
+//     addresses, the K tile needs none.  Six stages of each; the workgroup
+//     barrier is taken once every three steps.
 //   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 with both operands fp6 e2m3
 //     (exact for |code| <= 7, and twice the fp8 rate); every partial sum is
 //     an integer below 2^24, so the fp32 accumulator holds the exact integer
 //     score and no int->float conversion is needed.  Each lane holds one
-//     query column, so row max / row sum are in-lane (+1 cross-half swap).
+//     query column, so the row max is in-lane (+1 cross-half swap).
 //   * P codes come straight out of the accumulator registers: the distance
 //     of each score below the running max, rounded to the exponent grid, is
-//     turned into an index with one FMA, one add and one saturating subtract
-//     and looked up in a 46 KB table of 16-bit entries in LDS (u as e4m3 for
-//     the MFMA in the low byte, u as an integer for the row sum in the high
-//     byte), built per workgroup from the exp2 form of the map.  The e4m3
-//     bytes are packed in the order the PV MFMA wants them as its B operand;
-//     V is stored pre-permuted to match.
+//     turned into a table index by one clamped FMA and one multiply into the
+//     fp32 subnormal range (whose bit pattern is then the rounded index), and
+//     looked up in a 32 KB byte table of u as e4m3 at LDS address 0, built
+//     per workgroup from the exp2 form of the map.  Two byte permutes and an
+//     OR pack four codes in the order the PV MFMA wants them as its B
+//     operand; V is stored pre-permuted to match.
 //   * PV = V^T P^T also runs on the fp8 MFMA: u in [0, 15] and the V codes
 //     are exact in e4m3 and a step's sums are integers below 2^24, so each
 //     step's PV is exact; it accumulates across steps in fp32 registers,
 //     scaled by beta only when a query's running max rises (rare after the
-//     first few steps).
+//     first few steps).  The row sum of the codes is one more MFMA per step
+//     (16x16x128, the same P operand against an fp4 0/1 selector), so it
+//     costs no VALU work and lands in every lane that owns the query.
 #include <type_traits>
 
 #include "ra_common.h"
@@ -70,8 +72,7 @@ template <int D>
 struct State {
   v16f acc[Cfg<D>::DT];     // O^T: sum of u * vhat, scaled by beta when m rises
   float m;                  // running max (grid units), this lane's query
-  float L;                  // fp32 part of the row sum
-  uint32_t U;               // integer row sum of u since the last rescale (lane half)
+  v4f lsum;                 // row sum of u (16x16 MFMA accumulator; every register = this query's)
 };
 
 // ---- range-optimized P map through an LDS table --------------------------
@@ -82,25 +83,25 @@ struct State {
 // With c' = c 2^-15 and m' = m 2^-15 (exact power-of-two scalings):
 //   y = clamp(fma(S, -c', m'))   f32(m - S c) 2^-15 in [0, 1]: m >= max S c,
 //                                far keys saturate at 1, and with the DX10
-//                                clamp mode of compute kernels a NaN becomes
-//                                0, so y is in [0, 1] for every input
-//   w = y + 384                  the unit in the last place of 384 is 2^-15:
-//                                w = 384 + rint(f32(m - S c)) 2^-15 (round to
-//                                nearest even, as rint)
-//   a = 2 bits(w) - 2 bits(384)  byte offset of 16-bit entry j = -x, in
-//                                [0, 2^16] for every input
+//                                clamp mode of compute kernels a NaN or a
+//                                -0 becomes +0, so y is in [+0, 1] for
+//                                every input
+//   w = y 2^-134                 subnormal (f32 denormals are enabled in
+//                                these kernels), spacing 2^-149 = 2^-15 of
+//                                y: the product rounds f32(m - S c) to the
+//                                nearest integer, ties to even, as rint,
+//                                and bits(w) = -x = j in [0, 2^15]
+// The table sits at LDS address 0, so j is the byte address of its entry.
+// The running max is passed as m' + 0, which turns a -0 into +0.
 constexpr int kPTabSpan = 1 << 15;
-constexpr int kPTabEntries = kPTabSpan + 2;                 // j = 0..2^15, padded to 4 bytes
-constexpr int kPTabBytes = 2 * kPTabEntries;
+constexpr int kPTabEntries = kPTabSpan + 1;                 // j = 0..2^15
+constexpr int kPTabBytes = (kPTabEntries + 15) & ~15;       // one byte each, 16-byte padded
 constexpr float kPTabScale = 1.0f / 32768.0f;               // 2^-15
-constexpr uint32_t kPTabBias = 0u - 2u * 0x43C00000u;       // -2 bits(384) mod 2^32
-constexpr uint32_t kPTabZero = 2u * kPTabSpan;              // entry of j = 2^15: u = 0
 
 __device__ __forceinline__ uint32_t ptab_addr(float s, float c2, float m2) {
   float y;
   asm("v_fma_f32 %0, %1, -%2, %3 clamp" : "=v"(y) : "v"(s), "v"(c2), "v"(m2));
-  const float w = y + 384.0f;
-  return (__float_as_uint(w) << 1) + kPTabBias;
+  return __float_as_uint(y * 0x1p-134f);
 }
 
 // e4m3 encoding of an integer 0 <= u <= 15 (exact).
@@ -124,7 +125,7 @@ __device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt, int p_
   const float log2p = p_mode ? kLog2Of7 : kLog2Of15;
   for (int j = tid; j < kPTabEntries; j += nt) {
     const uint32_t u = pmap_insert(-(float)j, 0u, 0u, log2p) & 0xFFu;
-    reinterpret_cast<uint16_t*>(tab)[j] = (uint16_t)(e4m3_of_uint(u) | (u << 8));
+    tab[j] = (uint8_t)e4m3_of_uint(u);
   }
 }
 
@@ -236,24 +237,42 @@ __device__ __forceinline__ int acc_key(int mt, int r, int hf) {
   return mt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
 }
 
+// LDS address of a lane's base for one step's reads, hidden from the
+// optimizer: otherwise it splits stage + lane + constant offsets into one
+// loop-invariant register per read and re-adds the stage offset to each,
+// instead of one add per base and the constants in the read instructions.
+typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
+__device__ __forceinline__ lds_cu8* lds_base(const uint8_t* p) {
+  uint32_t a = (uint32_t)(uintptr_t)(lds_cu8*)p;
+  asm("" : "+v"(a));
+  return (lds_cu8*)(uintptr_t)a;
+}
+template <typename T>
+__device__ __forceinline__ T lds_ld(lds_cu8* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
+}
+
 // ---- building blocks of one 64-key step for the 32 queries of a wave ------
 
 // S^T of the step (exact integers in fp32): kst is the step's fp6 K tile.
 // Lane (ln, hf) supplies key row 32mt + ln, channel group 2qc + hf: one
 // 16-byte and one 8-byte LDS read, consecutive rows at consecutive
-// addresses (no bank conflicts without a swizzle).
+// addresses (no bank conflicts without a swizzle).  Both offsets are linear
+// in (row, group), so one lane base per part plus constants covers all reads.
 template <int D>
 __device__ __forceinline__ void qk_step(const uint8_t* kst, const v8i (&qop)[Cfg<D>::QC], v16f (&s)[2]) {
   const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
+  lds_cu8* const klo = lds_base(kst + qk6_lo_off(ln, hf));
+  lds_cu8* const khi = lds_base(kst + qk6_hi_off(D, ln, hf));
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[mt][r] = 0.0f;
 #pragma unroll
     for (int qc = 0; qc < Cfg<D>::QC; ++qc) {
-      const int row = mt * 32 + ln, g = 2 * qc + hf;
-      const v4i lo = *reinterpret_cast<const v4i*>(kst + qk6_lo_off(row, g));
-      const v2i hi = *reinterpret_cast<const v2i*>(kst + qk6_hi_off(D, row, g));
+      const int rg = 128 * qc + 32 * mt;   // (64 g + row) - (64 hf + ln)
+      const v4i lo = lds_ld<v4i>(klo + 16 * rg);
+      const v2i hi = lds_ld<v2i>(khi + 8 * rg);
       const v8i ka = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
       s[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qop[qc], s[mt], 2, 2, 0, 0, 0, 0);
     }
@@ -291,64 +310,71 @@ __device__ __forceinline__ float step_max(const v16f (&s)[2], float c) {
   return mul_round_up(mx, c);
 }
 
-// P codes of a whole step (u = code + 8 in e4m3, both M-tiles) in the order
-// of the PV MFMA's B operand: register 4i+e of M-tile mt goes to byte e of
-// p[mt][i].  U accumulates the integer u.  All 32 table loads are issued
-// before any is used, so the LDS latency is paid once per step; each pair of
-// 16-bit entries lands in the two halves of one register (e0 u0 e1 u1), and
-// one v_perm per four codes gathers the e4m3 bytes.
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
+// P codes of a whole step (u in e4m3, both M-tiles) in the order of the PV
+// MFMA's B operand: register 4i+e of M-tile mt goes to byte e of p[mt][i].
+// All 32 table loads are issued before any is used, so the LDS latency is
+// paid once per step; each load leaves one byte in the low end of its
+// register, and two v_perm (bytes 0-1 and 2-3) and an OR pack four of them.
 __device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c2, float m2, const uint8_t* tab,
-                                          uint32_t (&p)[2][4], uint32_t& U) {
-  uint32_t a[32];
+                                          uint32_t (&p)[2][4]) {
+  uint32_t x[32];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) a[k] = ptab_addr(s[k >> 4][k & 15], c2, m2);
-  uint32_t r[16];
+  for (int k = 0; k < 32; ++k) x[k] = tab[ptab_addr(s[k >> 4][k & 15], c2, m2)];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const u16x2 v = u16x2{*reinterpret_cast<const uint16_t*>(tab + a[2 * i]),
-                          *reinterpret_cast<const uint16_t*>(tab + a[2 * i + 1])};
-    r[i] = __builtin_bit_cast(uint32_t, v);
-  }
-  uint32_t us = 0u;   // bytes: partial sums of u, at most 8 x 15 each
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    p[w >> 2][w & 3] = __builtin_amdgcn_perm(r[2 * w + 1], r[2 * w], 0x06040200u);           // e0 e1 e2 e3
-    us += __builtin_amdgcn_perm(r[2 * w + 1], r[2 * w], 0x07050301u);
-  }
-  U = __builtin_amdgcn_sad_u8(us, 0u, U);
+  for (int w = 0; w < 8; ++w)
+    p[w >> 2][w & 3] = __builtin_amdgcn_perm(x[4 * w + 1], x[4 * w], 0x0C0C0400u) |
+                       __builtin_amdgcn_perm(x[4 * w + 3], x[4 * w + 2], 0x04000C0Cu);
 }
 
-// Padded keys of a ragged last step carry S = -inf.  With c > 0 they read
-// the last entry (u = 0); with c = 0 the product is NaN, which the clamp
-// turns into 0, so they read entry 0 (u = umax, the code of p = 1).  Their V
-// codes are 0, so only the row sum needs a correction: the u this lane's
-// padded keys added.
-__device__ __forceinline__ uint32_t padded_u(float c2, int nvalid, uint32_t umax) {
-  if (c2 != 0.0f) return 0u;
+// Zero the P codes of keys at or past nvalid (ragged last step).
+__device__ __forceinline__ void mask_p(uint32_t (&p)[2][4], int nvalid) {
   const int hf = (threadIdx.x & 63) >> 5;
-  int nv = 0;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) nv += min(max(nvalid - (32 * mt + 8 * g + 4 * hf), 0), 4);
-  return umax * (uint32_t)(32 - nv);
+    for (int g = 0; g < 4; ++g) {
+      const int n = min(max(nvalid - (32 * mt + 8 * g + 4 * hf), 0), 4);
+      p[mt][g] &= n >= 4 ? 0xFFFFFFFFu : ((1u << (8 * n)) - 1u);
+    }
+}
+
+// Row sums of the step's P codes on one 16x16x128 MFMA.  B = the PV operand:
+// lane l supplies column l % 16 with the 32 codes of query l % 32, so column
+// n holds query n in lane groups 0 and 2 and query n + 16 in groups 1 and 3.
+// A = fp4 0/1 selector.  An fp4 A lane covers, in registers 0-1, 16 K slots
+// of an even B lane group and, in registers 2-3, 16 slots of an odd one
+// (group 0: B groups 0 and 1, first 16 bytes; group 1: B groups 2 and 3,
+// first 16; groups 2 and 3: the same with the last 16 bytes), so rows r with
+// (r / 4) % 2 = 0 take ones in registers 0-1 and the others in registers
+// 2-3.  Output row r of column n then sums all 64 keys of query
+// n + 16 ((r / 4) % 2), the query of every lane that holds row r.
+__device__ __forceinline__ v8i lsum_selector() {
+  const int odd = (threadIdx.x >> 2) & 1;   // ((lane % 16) / 4) % 2
+  const int one = 0x22222222;                 // fp4 e2m1 1.0 = 0x2
+  return odd ? v8i{0, 0, one, one, 0, 0, 0, 0} : v8i{one, one, 0, 0, 0, 0, 0, 0};
+}
+__device__ __forceinline__ void lsum_step(const v8i& sel, const uint32_t (&p)[2][4], v4f& lsum) {
+  const v8i pb = v8i{(int)p[0][0], (int)p[0][1], (int)p[0][2], (int)p[0][3],
+                     (int)p[1][0], (int)p[1][1], (int)p[1][2], (int)p[1][3]};
+  lsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb, lsum, 4, 0, 0, 0, 0, 0);
 }
 
 // O^T += V^T P^T over the 64 keys of the step: lane half hf supplies slots
-// 32hf..32hf+31, i.e. 16-byte chunks 2hf and 2hf+1 of each V row.
+// 32hf..32hf+31, i.e. 16-byte chunks 2hf and 2hf+1 of each V row.  Rows
+// 32 dt + ln carry the swizzle of row ln (32 is a multiple of 16), so tile
+// dt lies 2048 dt bytes past the two lane bases.
 template <int D>
 __device__ __forceinline__ void pv_step(const uint8_t* vst, const uint32_t (&p)[2][4],
                                         v16f (&acc)[Cfg<D>::DT]) {
   const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const v8i pb = v8i{(int)p[0][0], (int)p[0][1], (int)p[0][2], (int)p[0][3],
                      (int)p[1][0], (int)p[1][1], (int)p[1][2], (int)p[1][3]};
+  lds_cu8* const v0p = lds_base(vst + swz64(ln, 2 * hf));
+  lds_cu8* const v1p = lds_base(vst + swz64(ln, 2 * hf + 1));
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
-    const int row = dt * 32 + ln;
-    const v4i v0 = *reinterpret_cast<const v4i*>(vst + swz64(row, 2 * hf));
-    const v4i v1 = *reinterpret_cast<const v4i*>(vst + swz64(row, 2 * hf + 1));
+    const v4i v0 = lds_ld<v4i>(v0p + 2048 * dt);
+    const v4i v1 = lds_ld<v4i>(v1p + 2048 * dt);
     const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[dt], 0, 0, 0, 0, 0, 0);
   }
@@ -363,8 +389,7 @@ __device__ __forceinline__ void rescale(State<D>& st, float m_new) {
   for (int dt = 0; dt < Cfg<D>::DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.acc[dt][r] *= beta;
-  st.L = (st.L + (float)st.U) * beta;
-  st.U = 0u;
+  st.lsum *= beta;
 }
 
 // c = f32(f32(s_q s_k) alpha_G): grid units per unit of integer score.
@@ -380,7 +405,6 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
                                           const v8i (&qop)[Cfg<D>::QC], float cq, float alpha_g,
                                           float sk, int nvalid, State<D>& st,
                                           const TileDumpArgs* dump, int wave, int p_mode) {
-  const uint32_t dump_umax = p_mode ? 7u : 15u;    // u of p = 1
   const int zp = p_mode ? 0 : 8;                   // code = u - zp
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
@@ -392,9 +416,10 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
   if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
   st.m = m_new;
   uint32_t p[2][4];
-  pmap_step(s, cp * kPTabScale, m_new * kPTabScale, tab, p, st.U);
-  if (nvalid < kBlock) st.U -= padded_u(cp * kPTabScale, nvalid, dump_umax);
+  pmap_step(s, cp * kPTabScale, m_new * kPTabScale + 0.0f, tab, p);
+  if (nvalid < kBlock) mask_p(p, nvalid);
   pv_step<D>(vst, p, st.acc);
+  lsum_step(lsum_selector(), p, st.lsum);
 
   if (DUMP) {
     // Exact per-step integers: S, P codes (decoded from the e4m3 operand
@@ -487,17 +512,16 @@ __device__ __forceinline__ void state_init(State<D>& st) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.acc[dt][r] = 0.0f;
   st.m = -INFINITY;
-  st.L = 0.0f;
-  st.U = 0u;
+  st.lsum = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 template <int D, bool OUT_BF16, bool VH>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * (C::KT + C::VT) + kPTabBytes];
-  uint8_t* const kbuf = smem;                     // K stages
-  uint8_t* const vbuf = smem + kStages * C::KT;   // V stages
-  uint8_t* const ptab = smem + kStages * (C::KT + C::VT);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPTabBytes + kStages * (C::KT + C::VT)];
+  uint8_t* const ptab = smem;                               // P-map table at LDS address 0
+  uint8_t* const kbuf = smem + kPTabBytes;                  // K stages
+  uint8_t* const vbuf = smem + kPTabBytes + kStages * C::KT;   // V stages
   ptab_build(ptab, threadIdx.x, 64 * kWaves, a.p_mode);     // visible after the first barrier
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
@@ -525,6 +549,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
 
   State<D> st;
   state_init<D>(st);
+  const v8i lsel = lsum_selector();
 
   // Step t: P codes of step t (S in registers), S of step t+1, P x V of step
   // t, then the running max of step t+1 and the rescale it may need.  Within
@@ -566,9 +591,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     dma.issue(t + kSync + 1 < nkb ? ktn : nullptr, t + kSync < nkb ? vtn : nullptr, kst(t + kSync + 1),
               vst(t + kSync));
     uint32_t p[2][4];
-    pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale, ptab, p, st.U);
+    pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale + 0.0f, ptab, p);
     qk_step<D>(kst(t + 1), qop, s);       // S of step t+1
     pv_step<D>(vst(t), p, st.acc);
+    lsum_step(lsel, p, st.lsum);
     if constexpr (decltype(ragged)::value) {
       const int nv1 = a.N - (t + 1) * kBlock;
       if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
@@ -600,17 +626,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     // The last step: its V tile is resident since the barrier before it.
     const int t = nkb - 1, nvalid = a.N - t * kBlock;
     uint32_t p[2][4];
-    pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale, ptab, p, st.U);
-    if (nvalid < kBlock) st.U -= padded_u(cp_cur * kPTabScale, nvalid, a.p_mode ? 7u : 15u);
+    pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale + 0.0f, ptab, p);
+    if (nvalid < kBlock) mask_p(p, nvalid);
     pv_step<D>(vst(t), p, st.acc);
+    lsum_step(lsel, p, st.lsum);
   }
 
   // o = A s_v / L: the scale of the dequantized P cancels against the
   // quantized row sum.  With the V-side Hadamard the V codes are of V H, and
   // the row is multiplied by H again.
-  const float lw = st.L + (float)st.U;
-  const float lt = xhalf_sum_f(lw);
-  const float inv = 1.0f / lt;
+  const float inv = 1.0f / st.lsum[0];
   if (VH) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -658,8 +683,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs t) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::KT + C::VT + kPTabBytes];
-  uint8_t* const ptab = smem + C::KT + C::VT;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPTabBytes + C::KT + C::VT];
+  uint8_t* const ptab = smem;
+  uint8_t* const tiles = smem + kPTabBytes;
   ptab_build(ptab, threadIdx.x, 128, a.p_mode);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const int bh = t.bh;
@@ -671,16 +697,16 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   state_init<D>(st);
   const TileDma<D, 2> dma;
   for (int kb = 0; kb <= t.kv_blk; ++kb) {
-    dma.issue(a.kp + ((size_t)bh * a.nblk + kb) * C::KT, a.vp + ((size_t)bh * a.nkb + kb) * C::VT, smem,
-              smem + C::KT);
+    dma.issue(a.kp + ((size_t)bh * a.nblk + kb) * C::KT, a.vp + ((size_t)bh * a.nkb + kb) * C::VT, tiles,
+              tiles + C::KT);
     wait_lds_dma();
     __syncthreads();
     const int nvalid = min(kBlock, a.N - kb * kBlock);
     const float sk = a.s_k[(size_t)bh * a.nblk + kb];
     if (kb == t.kv_blk)
-      tile_step<D, true>(smem, smem + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, &t, wave, a.p_mode);
+      tile_step<D, true>(tiles, tiles + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, &t, wave, a.p_mode);
     else
-      tile_step<D, false>(smem, smem + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave, a.p_mode);
+      tile_step<D, false>(tiles, tiles + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave, a.p_mode);
     __syncthreads();
   }
 }
@@ -694,7 +720,7 @@ __global__ __launch_bounds__(256) void k_pmap_probe(const float* __restrict__ x,
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
-    u[i] = (uint8_t)(*reinterpret_cast<const uint16_t*>(tab + ptab_addr(x[i], kPTabScale, 0.0f)) >> 8);
+    u[i] = (uint8_t)e4m3_to_uint(tab[ptab_addr(x[i], kPTabScale, 0.0f)]);
 }
 
 __global__ void k_copy16(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n16) {
