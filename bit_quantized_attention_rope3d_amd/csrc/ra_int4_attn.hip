@@ -298,16 +298,47 @@ __device__ __forceinline__ void mask_scores(v16f (&s)[2], int nvalid) {
       if (acc_key(mt, r, hf) >= nvalid) s[mt][r] = -INFINITY;
 }
 
+// Maxima as plain v_max3 / v_max: in IEEE mode the compiler brackets
+// fmaxf with NaN-quieting copies of its operands, and no value here is NaN
+// (scores are finite MFMA sums or -inf, running maxima are finite or -inf).
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// s * c rounded toward +infinity, i.e. the smallest float >= the exact
+// product: one multiply under the round-up mode of the fp32 rounding field
+// of MODE, set and restored to round-to-nearest-even around it within the
+// statement (two wait states after each mode write).
+__device__ __forceinline__ float mul_ru(float s, float c) {
+  float r;
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 1\n\t"
+      "s_nop 1\n\t"
+      "v_mul_f32 %0, %1, %2\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
+      "s_nop 1"
+      : "=v"(r)
+      : "v"(s), "v"(c));
+  return r;
+}
+
 // Running-max candidate of the step for this lane's query (grid units):
 // the smallest float >= max_j S_j * c.
 __device__ __forceinline__ float step_max(const v16f (&s)[2], float c) {
-  float mx = s[0][0];
+  float mx = vmax3(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-  mx = xhalf_max_f(mx);
-  return mul_round_up(mx, c);
+  for (int k = 3; k + 1 < 32; k += 2) mx = vmax3(mx, s[k >> 4][k & 15], s[(k + 1) >> 4][(k + 1) & 15]);
+  mx = vmax(mx, s[1][15]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+  mx = vmax(__int_as_float(r[0]), __int_as_float(r[1]));
+  return mul_ru(mx, c);
 }
 
 // P codes of a whole step (u in e4m3, both M-tiles) in the order of the PV
@@ -412,7 +443,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
   qk_step<D>(kst, qop, s);
   if (nvalid < kBlock) mask_scores(s, nvalid);
   const float cp = score_scale(cq, sk, alpha_g);
-  const float m_new = fmaxf(st.m, step_max(s, cp));
+  const float m_new = vmax(st.m, step_max(s, cp));
   if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
   st.m = m_new;
   uint32_t p[2][4];
@@ -600,7 +631,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
       if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
     }
     const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
-    const float m_new = fmaxf(st.m, step_max(s, cp_next));
+    const float m_new = vmax(st.m, step_max(s, cp_next));
     if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
     st.m = m_new;
     cp_cur = cp_next;
