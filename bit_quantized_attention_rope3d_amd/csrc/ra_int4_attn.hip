@@ -17,8 +17,8 @@
 //     bytes for D = 128) are copied from global memory straight into LDS by
 //     buffer loads with the LDS-direct bit (16 bytes per lane, no VGPRs, no
 //     VALU); the XOR swizzle of the V rows is applied through the source
-//     addresses, the K tile needs none.  Six stages of each; the workgroup
-//     barrier is taken once every three steps.
+//     addresses, the K tile needs none.  Eight stages of each; the
+//     workgroup barrier is taken once every four steps.
 //   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 with both operands fp6 e2m3
 //     (exact for |code| <= 7, and twice the fp8 rate); every partial sum is
 //     an integer below 2^24, so the fp32 accumulator holds the exact integer
@@ -48,7 +48,7 @@ namespace ra {
 
 constexpr int kWaves = 12;                 // waves per workgroup
 constexpr int kQTile = 32 * kWaves;        // query rows per workgroup
-constexpr int kSync = 3;                   // steps per workgroup barrier
+constexpr int kSync = 4;                   // steps per workgroup barrier
 constexpr int kStages = 2 * kSync;         // LDS stages of K and of V tiles
 
 template <int D>
