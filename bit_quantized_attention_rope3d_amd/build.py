@@ -3,7 +3,12 @@
 Usage: python -m bit_quantized_attention_rope3d_amd.build
 Every HIP source is compiled with -ffp-contract=off (the kernels request each
 fused multiply-add explicitly) and with packed-FP32 instruction selection
-disabled.
+disabled.  The INT4 attention kernels are also compiled without NaN semantics:
+no value they compare or take the maximum of is NaN (scores are finite MFMA
+sums or -inf, running maxima finite or -inf), and with them the compiler
+would wrap every fmaxf in NaN-quieting copies of its operands.  The one NaN
+the P map can form (0 * inf for a masked key of a zero-scale block) goes
+through the FMA's clamp bit, which the hardware maps to 0.
 """
 from __future__ import annotations
 
@@ -22,6 +27,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["ra_host.cpp", "ra_prologue.hip", "ra_int4_attn.hip", "ra_bf16_attn.hip"]
+EXTRA = {"ra_int4_attn.hip": ["-fno-honor-nans"]}
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
@@ -34,7 +40,7 @@ CFLAGS = [
 
 def _compile(src: str, extra=()) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, ()), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

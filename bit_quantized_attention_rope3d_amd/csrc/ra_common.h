@@ -92,19 +92,6 @@ __device__ __forceinline__ uint32_t pmap_insert(float x, uint32_t sel, uint32_t 
   return __builtin_amdgcn_cvt_pk_u8_f32(y, sel, acc);
 }
 
-// Smallest float >= the exact product s * c (c finite, s an integer-valued
-// float with |s| < 2^24).
-__device__ __forceinline__ float mul_round_up(float s, float c) {
-  float m = s * c;
-  float r = __builtin_fmaf(s, c, -m);
-  if (r > 0.0f) {
-    uint32_t b = __float_as_uint(m);
-    b = (m > 0.0f) ? b + 1u : (m < 0.0f ? b - 1u : 1u);
-    m = __uint_as_float(b);
-  }
-  return m;
-}
-
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }

@@ -81,11 +81,14 @@ struct State {
 // exponent is x = rint(f32(S c - m)) <= 0 and the code is u(x); u(x) = 0 for
 // every x <= -2^15, so a table of u(-j), j = 0..2^15, covers all scores.
 // With c' = c 2^-15 and m' = m 2^-15 (exact power-of-two scalings):
-//   y = clamp(fma(S, -c', m'))   f32(m - S c) 2^-15 in [0, 1]: m >= max S c,
-//                                far keys saturate at 1, and with the DX10
-//                                clamp mode of compute kernels a NaN or a
-//                                -0 becomes +0, so y is in [+0, 1] for
-//                                every input
+//   y = clamp(fma(S, -c', m'))   f32(m - S c) 2^-15 clamped to [0, 1]:
+//                                keys at or above the running max (the
+//                                scaled max rounded to nearest, so a key
+//                                may exceed it by half an ulp) give 0, the
+//                                top code, far keys saturate at 1, and with
+//                                the DX10 clamp mode of compute kernels a
+//                                NaN or a -0 becomes +0, so y is in [+0, 1]
+//                                for every input
 //   w = y 2^-134                 subnormal (f32 denormals are enabled in
 //                                these kernels), spacing 2^-149 = 2^-15 of
 //                                y: the product rounds f32(m - S c) to the
@@ -99,8 +102,8 @@ constexpr int kPTabBytes = (kPTabEntries + 15) & ~15;       // one byte each, 16
 constexpr float kPTabScale = 1.0f / 32768.0f;               // 2^-15
 
 __device__ __forceinline__ uint32_t ptab_addr(float s, float c2, float m2) {
-  float y;
-  asm("v_fma_f32 %0, %1, -%2, %3 clamp" : "=v"(y) : "v"(s), "v"(c2), "v"(m2));
+  // med3(x, 0, 1) folds into the clamp bit of the FMA (DX10 clamp mode).
+  const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(s, -c2, m2), 0.0f, 1.0f);
   return __float_as_uint(y * 0x1p-134f);
 }
 
@@ -298,47 +301,13 @@ __device__ __forceinline__ void mask_scores(v16f (&s)[2], int nvalid) {
       if (acc_key(mt, r, hf) >= nvalid) s[mt][r] = -INFINITY;
 }
 
-// Maxima as plain v_max3 / v_max: in IEEE mode the compiler brackets
-// fmaxf with NaN-quieting copies of its operands, and no value here is NaN
-// (scores are finite MFMA sums or -inf, running maxima are finite or -inf).
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float vmax(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
-// s * c rounded toward +infinity, i.e. the smallest float >= the exact
-// product: one multiply under the round-up mode of the fp32 rounding field
-// of MODE, set and restored to round-to-nearest-even around it within the
-// statement (two wait states after each mode write).
-__device__ __forceinline__ float mul_ru(float s, float c) {
-  float r;
-  asm volatile(
-      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 1\n\t"
-      "s_nop 1\n\t"
-      "v_mul_f32 %0, %1, %2\n\t"
-      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
-      "s_nop 1"
-      : "=v"(r)
-      : "v"(s), "v"(c));
-  return r;
-}
-
-// Running-max candidate of the step for this lane's query (grid units):
-// the smallest float >= max_j S_j * c.
-__device__ __forceinline__ float step_max(const v16f (&s)[2], float c) {
-  float mx = vmax3(s[0][0], s[0][1], s[0][2]);
+// New running max for this lane's query (grid units): the larger of m and
+// f32(max_j S_j * c), rounded to nearest.
+__device__ __forceinline__ float running_max(const v16f (&s)[2], float c, float m) {
+  float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-  for (int k = 3; k + 1 < 32; k += 2) mx = vmax3(mx, s[k >> 4][k & 15], s[(k + 1) >> 4][(k + 1) & 15]);
-  mx = vmax(mx, s[1][15]);
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
-  mx = vmax(__int_as_float(r[0]), __int_as_float(r[1]));
-  return mul_ru(mx, c);
+  for (int k = 2; k < 32; ++k) mx = fmaxf(mx, s[k >> 4][k & 15]);
+  return fmaxf(m, xhalf_max_f(mx) * c);
 }
 
 // P codes of a whole step (u in e4m3, both M-tiles) in the order of the PV
@@ -443,7 +412,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
   qk_step<D>(kst, qop, s);
   if (nvalid < kBlock) mask_scores(s, nvalid);
   const float cp = score_scale(cq, sk, alpha_g);
-  const float m_new = vmax(st.m, step_max(s, cp));
+  const float m_new = running_max(s, cp, st.m);
   if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
   st.m = m_new;
   uint32_t p[2][4];
@@ -612,7 +581,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     if (nv0 < kBlock) mask_scores(s, nv0);
   }
   float cp_cur = score_scale(cq, sk[0], a.alpha_g);
-  st.m = step_max(s, cp_cur);
+  st.m = running_max(s, cp_cur, -INFINITY);
   wait_lds_dma();
   __syncthreads();
   const uint8_t* ktn = ktiles + (kSync + 1) * C::KT;   // K tile of step t + kSync + 1
@@ -631,7 +600,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
       if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
     }
     const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
-    const float m_new = vmax(st.m, step_max(s, cp_next));
+    const float m_new = running_max(s, cp_next, st.m);
     if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
     st.m = m_new;
     cp_cur = cp_next;

@@ -343,15 +343,6 @@ int ora_pmap_p(const float *x, int64_t n, int p_mode, uint8_t *u)
 
 int ora_pmap(const float *x, int64_t n, uint8_t *u) { return ora_pmap_p(x, n, 0, u); }
 
-/* Smallest binary32 value >= the exact product s * c (s integer, |s| < 2^24). */
-static float mul_round_up(int32_t s, float c)
-{
-    double exact = (double)s * (double)c;        /* exact: 24 + 24 bits */
-    float m = (float)exact;
-    if ((double)m < exact) m = nextafterf(m, INFINITY);
-    return m;
-}
-
 /* ------------------------------------------------------------------------ */
 /* INT4 attention for one (b, h) slice, on selected query rows.
  *
@@ -361,8 +352,10 @@ static float mul_round_up(int32_t s, float c)
  *   scores     S = sum_d qhat kc                               (exact int)
  *   c          = f32(f32(s_q s_k) * alphaG),
  *              alphaG = f32(log2(e) * softmax_scale * G)       (log2 units * G)
- *   step max   m_t = smallest f32 >= max_j(S_j) * c;  m = max(m, m_t)
- *   exponent   x_j = RNE(f32(S_j c - m))  (single rounding of the exact value)
+ *   step max   m_t = f32(max_j(S_j) * c), rounded to nearest;  m = max(m, m_t)
+ *   exponent   x_j = RNE(f32(S_j c - m))  (single rounding of the exact value);
+ *              a key whose S_j c lies above m (by at most half an ulp of m)
+ *              has x_j >= 0 and, like the max itself, the top code
  *   P code     u_j = #{k : x_j >= tau_k}  in [0, 15]; code = u - 8
  *              (p_mode 1, symmetric: u_j in [0, 7], code = u, zero-point 0)
  *   sums       U = sum_j u_j;  num_c = sum_j u_j vhat_jc;
@@ -419,7 +412,7 @@ int ora_attention_head(const int8_t *qc, const float *sq,
                 S[j] = (int32_t)acc;
                 if (S[j] > smax) smax = S[j];
             }
-            float mt = mul_round_up(smax, c);
+            float mt = (float)((double)smax * (double)c);   /* exact product, one rounding */
             float mnew = m > mt ? m : mt;
 
             int64_t U = 0;

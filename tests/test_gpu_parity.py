@@ -175,6 +175,36 @@ def test_zero_scale_blocks(ora, p_mode):
         assert np.array_equal(g["m_after"][:n].view(np.uint32), t["m_after"].view(np.uint32)), (qb, kb, "m")
 
 
+def test_large_scores(ora):
+    """Q and K scaled by 16 make the score scale c 256 times larger, so the
+    step max m = f32(S_max c) has an ulp of hundreds of grid units and can
+    round below S_max c: those keys have a positive grid exponent and the top
+    code.  The codes and the running max must still match the oracle bit for
+    bit.  (Far larger scales make the f32 grid exponent too coarse to keep
+    any code above 0, on both sides alike.)"""
+    w = CASES["medium"].with_(name="large", dtype="f32")
+    q, k, v, _ = inputs.generate(w)
+    q *= np.float32(16.0)
+    k *= np.float32(16.0)
+    pro = ora.prologue(q, k, v, w.grid, w.seg, w.theta, w.rot_id)
+    p = plan_for(w)
+    o = p.forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    want = ora.attention_full(pro)
+    err, cos = np.abs(o - want).max(), cosine(o, want)
+    say("large scores: max|gpu-oracle| %.2e cos %.7f" % (err, cos))
+    assert err <= 2e-3 and cos >= 0.999
+    ws = p.workspace()
+    p.prologue(dev(q), dev(k), dev(v), ws)
+    nb = (w.tokens + 63) // 64
+    for qb, kb in [(0, 0), (3, 7), (nb - 1, nb - 1), (5, nb - 1)]:
+        g = p.debug_tile(ws, 0, 1, qb, kb)
+        t = ora.attention_tile(pro, 0, 1, qb, kb)
+        n = t["s_int"].shape[0]
+        assert np.array_equal(g["p_code"][:n], t["p_code"]), (qb, kb, "P")
+        assert np.array_equal(g["pv_int"][:n], t["pv_int"]), (qb, kb, "PV")
+        assert np.array_equal(g["m_after"][:n].view(np.uint32), t["m_after"].view(np.uint32)), (qb, kb, "m")
+
+
 def test_deterministic(ora):
     w = CASES["medium"]
     q, k, v, _ = inputs.generate(w)

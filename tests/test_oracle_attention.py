@@ -29,9 +29,9 @@ def _alpha_g(ora, D):
     return np.float32(np.log2(np.e) * (1.0 / np.sqrt(D)) * ora.pgrid())
 
 
-def _ru32(exact):
-    m = np.float32(exact)
-    return np.nextafter(m, np.float32(np.inf)) if float(m) < exact else m
+def _rn32(exact):
+    """The running max of a step: the scaled max score rounded to nearest."""
+    return np.float32(exact)
 
 
 def test_zero_queries_give_channel_means(ora):
@@ -100,8 +100,8 @@ def test_two_tiles_of_equal_scores(ora, order):
     v1 = vc[64:].sum(axis=0).astype(np.float64)
     for qb in range(2):
         c = np.float32(np.float32(sq[qb] * sk[0]) * _alpha_g(ora, D))
-        m0 = _ru32(a * float(c))
-        m1 = _ru32(b * float(c))
+        m0 = _rn32(a * float(c))
+        m1 = _rn32(b * float(c))
         rows = slice(qb * 64, qb * 64 + 64)
         if order == "rising":
             beta = 2.0 ** ((float(m0) - float(m1)) / G)
@@ -114,6 +114,47 @@ def test_two_tiles_of_equal_scores(ora, order):
             want = (15 * v0 + u1 * v1) / (15 * 64 + u1 * 64)
             assert np.all(m[rows] == m0)
         assert np.allclose(o[rows], (sv * want)[None, :], rtol=1e-13)
+
+
+def test_keys_above_the_rounded_max_get_the_top_code(ora):
+    """The step max is m = f32(S_max c), rounded to nearest.  With a large
+    score scale c it is coarse (an ulp of 8 grid units or more) and may lie
+    below S_max c; the max key then has x = rint(f32(S_max c - m)) >= 1 and
+    still gets the top code 15 - 8 = 7, while a key one score lower is
+    mapped against m as usual."""
+    D, N = 64, 64
+    qc = np.zeros((N, D), int)
+    qc[:, 0] = 7
+    qc[:, 1] = 1
+    kc = np.zeros((N, D), int)
+    kc[:, 0] = -7                      # background keys: S = -49
+    kc[3, 0] = 7                       # S = 49
+    kc[9, 0] = 7
+    kc[9, 1] = -1                      # S = 48
+    rng = np.random.default_rng(21)
+    vc = rng.integers(-7, 8, size=(N, D))
+    alpha = np.float32(_alpha_g(ora, D))
+    G = ora.pgrid()
+    picked = None
+    for i in range(400):
+        s = np.float32(np.sqrt(2.0 ** 26 / (49 * float(alpha))) * (1.0 + i * 1e-4))
+        c = np.float32(np.float32(s * s) * alpha)
+        exact = 49.0 * float(c)
+        m = _rn32(exact)
+        x3 = np.rint(np.float32(exact - float(m)))
+        if float(m) < exact and x3 >= 1 and float(np.spacing(m)) >= 8.0:
+            picked = (s, c, m)
+            break
+    assert picked is not None
+    s, c, m = picked
+    pro = _pro(qc, kc, vc, sq=[s], sk=[s])
+    t = ora.attention_tile(pro, 0, 0, 0, 0)
+    assert np.all(t["m_after"] == m)
+    assert np.all(t["p_code"][:, 3] == 7)
+    x9 = np.rint(np.float32(48.0 * float(c) - float(m)))
+    u9 = int(np.floor(15 * 2.0 ** (float(x9) / G) + 0.5)) if x9 < 0 else 15
+    assert np.all(t["p_code"][:, 9] == u9 - 8)
+    assert np.all(t["p_code"][:, 0] == -8)
 
 
 def test_tile_dump_integers(ora):
