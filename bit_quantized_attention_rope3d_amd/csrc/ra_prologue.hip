@@ -12,6 +12,8 @@
 // All kernels are HBM-bound streaming passes; every workgroup reads a 64-token
 // x D tile once (16-byte loads), does the arithmetic in fp32 registers/LDS and
 // writes packed output with 16-byte stores.
+#include <type_traits>
+
 #include "ra_common.h"
 #include "ra_kernels.h"
 
@@ -235,15 +237,23 @@ __global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
   // Pass 1: all rows' loads and RoPE, with no barrier in between, so every
   // load of the wave's 16 rows (inputs and table entries) is in flight at
   // once.
+  // Blocks that lie wholly inside N (all but the ragged last one) skip the
+  // per-row bounds check.
   float y[ITERS][2];
+  const size_t row0 = ((size_t)b * a.N + (size_t)blk * kBlock + r0) * a.H + h;   // [B, N, H] row index
+  auto pass1 = [&](auto check) {
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const int n = blk * kBlock + r0 + it * PL::RPI;
-    float x0 = 0.0f, x1 = 0.0f;
-    if (n < a.N) load_pair<BF16>(x, (((size_t)b * a.N + n) * a.H + h) * D + 2 * pl.j, x0, x1);
-    pl.rope(n < a.N ? gp.axis(pl.s) : 0, x0, x1, y[it][0], y[it][1]);
-    gp.advance(PL::RPI, a.tabs);
-  }
+    for (int it = 0; it < ITERS; ++it) {
+      const int n = blk * kBlock + r0 + it * PL::RPI;
+      const bool ok = !decltype(check)::value || n < a.N;
+      float x0 = 0.0f, x1 = 0.0f;
+      if (ok) load_pair<BF16>(x, (row0 + (size_t)it * PL::RPI * a.H) * D + 2 * pl.j, x0, x1);
+      pl.rope(ok ? gp.axis(pl.s) : 0, x0, x1, y[it][0], y[it][1]);
+      gp.advance(PL::RPI, a.tabs);
+    }
+  };
+  if ((blk + 1) * kBlock <= a.N) pass1(std::false_type{});
+  else pass1(std::true_type{});
   // Pass 2 (Half): the partner of channel i of a segment, i +- L/2, is read
   // from the lane holding it with a cross-lane permute (no LDS allocation).
   // With L/2 even the partners of both channels of a pair sit at the same
@@ -419,18 +429,25 @@ __global__ __launch_bounds__(256) void k_rope_bf16(QKPrologueArgs a) {
   const PL pl(a.tabs);
   const int r0 = wave * 16 + pl.sub;
   GridPos gp(blk * kBlock + r0, a.tabs);
+  const size_t row0 = ((size_t)b * a.N + (size_t)blk * kBlock + r0) * a.H + h;   // [B, N, H] row index
+  // As in k_rope_quant_qk: no per-row bounds check on whole blocks.
+  auto rows = [&](auto check) {
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const int r = r0 + it * PL::RPI;
-    const int n = blk * kBlock + r;
-    float x0 = 0.0f, x1 = 0.0f;
-    if (n < a.N) load_pair<BF16>(x, (((size_t)b * a.N + n) * a.H + h) * D + 2 * pl.j, x0, x1);
-    float v0, v1;
-    pl.rope(n < a.N ? gp.axis(pl.s) : 0, x0, x1, v0, v1);
-    *reinterpret_cast<uint32_t*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + 2 * pl.j) =
-        (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
-    gp.advance(PL::RPI, a.tabs);
-  }
+    for (int it = 0; it < ITERS; ++it) {
+      const int r = r0 + it * PL::RPI;
+      const int n = blk * kBlock + r;
+      const bool ok = !decltype(check)::value || n < a.N;
+      float x0 = 0.0f, x1 = 0.0f;
+      if (ok) load_pair<BF16>(x, (row0 + (size_t)it * PL::RPI * a.H) * D + 2 * pl.j, x0, x1);
+      float v0, v1;
+      pl.rope(ok ? gp.axis(pl.s) : 0, x0, x1, v0, v1);
+      *reinterpret_cast<uint32_t*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + 2 * pl.j) =
+          (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+      gp.advance(PL::RPI, a.tabs);
+    }
+  };
+  if ((blk + 1) * kBlock <= a.N) rows(std::false_type{});
+  else rows(std::true_type{});
 }
 
 // V for the bf16 path: per 64-key block, [d][64 slots] bf16 in the bf16 PV
