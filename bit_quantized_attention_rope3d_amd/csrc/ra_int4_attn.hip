@@ -540,10 +540,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   v8i qop[C::QC];
   load_q<D>(a, bh, q0 + ln, hf, qop);
   const float cq = qblk < a.nblk ? a.s_q[(size_t)bh * a.nblk + qblk] : 0.0f;
-  // K scales are read-only here and indexed by the (uniform) step: reading
-  // them through the constant address space makes them scalar loads, so
-  // waiting for one never waits on the vector-memory counter that tracks
-  // the K/V tile copies.
+  // K scales of this (b, h), one per key step, read through the constant
+  // address space (the compiler still emits a vector load).  Each step loads
+  // the next one, and waiting for it also waits for the tile copies the step
+  // has issued; loading a block's scales ahead of its barrier, or through
+  // scalar loads, measured slower.
   const __attribute__((address_space(4))) float* sk =
       (const __attribute__((address_space(4))) float*)(a.s_k + (size_t)bh * a.nblk);
 
