@@ -243,16 +243,16 @@ def main():
         del wsb, outb
         pb.close()
 
-    # Prologue: algorithmic bytes (bf16 Q, K, V read once; Q and K codes
-    # written as 6-bit fp6, V codes as one byte).
+    # Prologue: algorithmic bytes (bf16 Q, K, V read once; Q, K and V codes
+    # written as 6-bit fp6).
     E = w.batch * w.tokens * w.heads * w.head_dim
-    pro_bytes = 3 * E * 2 + 2 * E * 3 // 4 + E
+    pro_bytes = 3 * E * 2 + 3 * E * 3 // 4
     traffic = traffic_for_current_kernel()
     roof = dict(bound="mfma", achieved=achieved_main, peak=MIXED_PEAK_TFLOPS, unit="TFLOP/s",
                 frac=achieved_main / MIXED_PEAK_TFLOPS, traffic=traffic,
                 kernel="int4_flash_fwd (k_int4_attn<128>)", avg_launch_ms=main_avg,
                 ops_per_launch=ops, note="multiply-adds counted as 2 ops; QK^T (half the ops) "
-                "runs on the fp6 MFMA (10.1 PFLOP/s dense) and PV on the fp8 MFMA (5.0), so "
+                "runs on the fp6 MFMA (10.1 PFLOP/s dense) and PV (fp6 V x fp8 P) at the fp8 rate (5.0), so "
                 "peak = 2 / (1/10.1 + 1/5.0) PFLOP/s = %.0f TFLOP/s; pct_int8_peak is the same "
                 "throughput against the 5.0 POP/s INT8 peak" % MIXED_PEAK_TFLOPS)
 

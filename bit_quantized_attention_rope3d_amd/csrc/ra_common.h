@@ -35,7 +35,7 @@ constexpr float kLog2Of7 = (float)2.8073549220576042;
 // attention kernels (readers).  gfx950 has no INT4 matrix instruction, so
 // every INT4 code (Q, K, V in [-7, 7]) is stored already in the operand
 // format of the f8f6f4 MFMA that consumes it, chosen once here rather than
-// converted in each query tile of the attention.  Both encodings are exact
+// converted in each query tile of the attention: fp6 e2m3, which is exact
 // for integers in [-7, 7].
 //   * Q/K: fp6 e2m3 (6 bits per code), in tiles of 64 tokens (one scale
 //     block).  A tile holds D/32 channel groups; the 32 codes of (token r,
@@ -45,16 +45,31 @@ constexpr float kLog2Of7 = (float)2.8073549220576042;
 //     the 8 bytes at (D/32) * 1024 + (64 g + r) * 8: one 64-token tile is
 //     48 * D bytes, read with one 16-byte and one 8-byte access per lane,
 //     consecutive tokens at consecutive addresses.
-//   * V tile of one 64-key block: fp8 e4m3 bytes; for each channel d, 64
-//     bytes holding the 64 key slots in MFMA operand order.
+//   * V: fp6 e2m3 tiles of one 64-key block (below, v6_*), the codes of
+//     each channel in the slot order of the PV MFMA.
 //   Slot s = 32*hf + 16*mt + j (j < 16) carries key 32*mt + 8*(j/4) + 4*hf +
 //   (j%4): the key that the 32x32 accumulator of M-tile mt of S^T = K Q^T
-//   leaves in register j of lane half hf.  Lane half hf supplies K-elements
-//   32*hf..32*hf+31 of the PV MFMA's B operand, so the P codes of a lane are
-//   that operand as they stand, with no shuffle.
+//   leaves in register j of lane half hf.  Lane half hf supplies the bytes
+//   of slots 32*hf..32*hf+31 of the PV MFMA's fp8 B operand, so the P codes
+//   of a lane are that operand as they stand, with no shuffle.
 __host__ __device__ constexpr int qk6_tile_bytes(int D) { return 48 * D; }
 __host__ __device__ constexpr int qk6_lo_off(int r, int g) { return (64 * g + r) * 16; }
 __host__ __device__ constexpr int qk6_hi_off(int D, int r, int g) { return (D / 32) * 1024 + (64 * g + r) * 8; }
+
+// V tile of one 64-key block in fp6 e2m3, the A operand of the PV MFMA
+// (whose B operand, the P codes, is fp8).  For channel d and lane half hf
+// the 32 codes one lane supplies form 192 bits, code f at bits [6f, 6f+6):
+// bits 0..127 at (D hf + d) * 16, bits 128..191 at 32 D + (D hf + d) * 8;
+// 48 D bytes per tile, consecutive channels at consecutive addresses.  In
+// this mixed fp6 x fp8 product, code f of lane half hf meets the P byte of
+// slot 32 (f / 16) + 16 hf + f % 16 (lane layout of
+// v_mfma_f32_32x32x64_f8f6f4 with an fp6 A and an fp8 B operand, measured
+// with a probe: a lane half of the fp6 operand covers 16-slot pieces of
+// both halves of the fp8 one).
+__host__ __device__ constexpr int v6_tile_bytes(int D) { return 48 * D; }
+__host__ __device__ constexpr int v6_lo_off(int D, int d, int hf) { return (D * hf + d) * 16; }
+__host__ __device__ constexpr int v6_hi_off(int D, int d, int hf) { return 32 * D + (D * hf + d) * 8; }
+__host__ __device__ constexpr int v6_slot(int hf, int f) { return 32 * (f >> 4) + 16 * hf + (f & 15); }
 
 __host__ __device__ constexpr int slot_key_pv(int slot) {
   return 32 * ((slot >> 4) & 1) + 8 * ((slot & 15) >> 2) + 4 * (slot >> 5) + (slot & 3);

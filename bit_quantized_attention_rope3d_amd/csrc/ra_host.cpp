@@ -107,7 +107,7 @@ Layout layout_of(const ra_shape* s, const ra_opts* o) {
   size_t off = 0;
   if (o->prec == RA_PREC_INT4) {
     const size_t qk = BH * L.nblk * (size_t)ra::qk6_tile_bytes((int)D);   // fp6 tiles
-    const size_t vb = BH * L.Npad * D;                                     // one e4m3 byte per code
+    const size_t vb = BH * L.nkb * (size_t)ra::v6_tile_bytes((int)D);     // fp6 tiles
     L.off_q = off; off = align_up(off + qk, A);
     L.off_k = off; off = align_up(off + qk, A);
     L.off_v = off; off = align_up(off + vb, A);
@@ -464,7 +464,7 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
   const Layout& L = p->lay;
   const size_t BH = (size_t)p->shape.batch * p->shape.heads;
   const int D = p->shape.head_dim, N = L.N;
-  const size_t qkb = BH * L.nblk * (size_t)ra::qk6_tile_bytes(D), tens = BH * L.Npad * D;
+  const size_t qkb = BH * L.nblk * (size_t)ra::qk6_tile_bytes(D), tens = BH * L.nkb * (size_t)ra::v6_tile_bytes(D);
   std::vector<uint8_t> pq(qkb), pk(qkb), pv(tens);
   const uint8_t* w = static_cast<const uint8_t*>(ws);
   if (hipMemcpy(pq.data(), w + L.off_q, qkb, hipMemcpyDeviceToHost) != hipSuccess ||
@@ -476,13 +476,18 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
     return fail(RA_ERR_HIP, "copy of prologue outputs failed");
   // Encoded code -> integer code; encodings of no code in [-7, 7] decode to
   // -128, which no valid code equals.
-  int8_t code_of[256], code_of6[64];
-  for (int i = 0; i < 256; ++i) code_of[i] = INT8_MIN;
+  int8_t code_of6[64];
   for (int i = 0; i < 64; ++i) code_of6[i] = INT8_MIN;
-  for (int c = -7; c <= 7; ++c) {
-    code_of[ra::e4m3_of_code(c)] = (int8_t)c;
-    code_of6[ra::e2m3_of_code(c)] = (int8_t)c;
-  }
+  for (int c = -7; c <= 7; ++c) code_of6[ra::e2m3_of_code(c)] = (int8_t)c;
+  // Code i of a 192-bit fp6 string (16 bytes, then 8).
+  auto fp6_code = [&](const uint8_t* lo, const uint8_t* hi, int i) {
+    uint8_t bits[24];
+    std::memcpy(bits, lo, 16);
+    std::memcpy(bits + 16, hi, 8);
+    const int b0 = 6 * i;
+    const unsigned v = (unsigned)bits[b0 / 8] | ((unsigned)(b0 / 8 + 1 < 24 ? bits[b0 / 8 + 1] : 0) << 8);
+    return code_of6[(v >> (b0 % 8)) & 0x3Fu];
+  };
   // Q/K: fp6 tiles of 64 tokens; (token r, group g) is 192 bits, code i at
   // bits [6i, 6i+6): 16 bytes at the lo offset, then 8 at the hi offset.
   const int tb = ra::qk6_tile_bytes(D);
@@ -493,27 +498,23 @@ ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void*
       for (int g = 0; g < D / 32; ++g)
         for (int which = 0; which < 2; ++which) {
           const uint8_t* t = (which ? pk.data() : pq.data()) + tile;
-          uint8_t bits[24];
-          std::memcpy(bits, t + ra::qk6_lo_off(r, g), 16);
-          std::memcpy(bits + 16, t + ra::qk6_hi_off(D, r, g), 8);
           int8_t* o = (which ? k_codes : q_codes) + (bh * N + n) * D + 32 * g;
-          for (int i = 0; i < 32; ++i) {
-            const int b0 = 6 * i;
-            const unsigned v = (unsigned)bits[b0 / 8] | ((unsigned)(b0 / 8 + 1 < 24 ? bits[b0 / 8 + 1] : 0) << 8);
-            o[i] = code_of6[(v >> (b0 % 8)) & 0x3Fu];
-          }
+          for (int i = 0; i < 32; ++i) o[i] = fp6_code(t + ra::qk6_lo_off(r, g), t + ra::qk6_hi_off(D, r, g), i);
         }
     }
-  // V: per 64-key block and channel, 64 slots in operand order.
+  // V: per 64-key block, channel and lane half, 32 codes whose slots follow
+  // the fp6 x fp8 lane layout of the PV MFMA.
   for (size_t bh = 0; bh < BH; ++bh)
-    for (int kb = 0; kb < L.nkb; ++kb)
-      for (int d = 0; d < D; ++d) {
-        const uint8_t* r = pv.data() + ((bh * L.nkb + kb) * D + d) * 64;
-        for (int slot = 0; slot < 64; ++slot) {
-          const int key = kb * 64 + ra::slot_key_pv(slot);
-          if (key < N) v_codes[(bh * N + key) * D + d] = code_of[r[slot]];
-        }
-      }
+    for (int kb = 0; kb < L.nkb; ++kb) {
+      const uint8_t* t = pv.data() + (bh * L.nkb + kb) * (size_t)ra::v6_tile_bytes(D);
+      for (int d = 0; d < D; ++d)
+        for (int hf = 0; hf < 2; ++hf)
+          for (int f = 0; f < 32; ++f) {
+            const int key = kb * 64 + ra::slot_key_pv(ra::v6_slot(hf, f));
+            if (key < N)
+              v_codes[(bh * N + key) * D + d] = fp6_code(t + ra::v6_lo_off(D, d, hf), t + ra::v6_hi_off(D, d, hf), f);
+          }
+    }
   return ok();
 }
 

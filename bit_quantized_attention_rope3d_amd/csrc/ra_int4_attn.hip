@@ -13,12 +13,11 @@
 //     and hide one another's LDS and matrix-core latencies (one workgroup per
 //     CU).  Workgroup ids are remapped so that the workgroups resident on one
 //     XCD walk the same head, sharing K/V tiles in that XCD's L2.
-//   * Per 64-key step the K and V code tiles (6 KB of fp6 + 8 KB of e4m3
-//     bytes for D = 128) are copied from global memory straight into LDS by
-//     buffer loads with the LDS-direct bit (16 bytes per lane, no VGPRs, no
-//     VALU); the XOR swizzle of the V rows is applied through the source
-//     addresses, the K tile needs none.  Eight stages of each; the
-//     workgroup barrier is taken once every four steps.
+//   * Per 64-key step the K and V code tiles (6 KB of fp6 each for D = 128)
+//     are copied from global memory straight into LDS by buffer loads with
+//     the LDS-direct bit (16 bytes per lane, no VGPRs, no VALU), as they lie.
+//     Eight stages of each; the workgroup barrier is taken once every four
+//     steps.
 //   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 with both operands fp6 e2m3
 //     (exact for |code| <= 7, and twice the fp8 rate); every partial sum is
 //     an integer below 2^24, so the fp32 accumulator holds the exact integer
@@ -32,13 +31,13 @@
 //     per workgroup from the exp2 form of the map.  Two byte permutes and an
 //     OR pack four codes in the order the PV MFMA wants them as its B
 //     operand; V is stored pre-permuted to match.
-//   * PV = V^T P^T also runs on the fp8 MFMA: u in [0, 15] and the V codes
-//     are exact in e4m3 and a step's sums are integers below 2^24, so each
-//     step's PV is exact; it accumulates across steps in fp32 registers,
-//     scaled by beta only when a query's running max rises (rare after the
-//     first few steps).  The row sum of the codes is one more MFMA per step
-//     (16x16x128, the same P operand against an fp4 0/1 selector), so it
-//     costs no VALU work and lands in every lane that owns the query.
+//   * PV = V^T P^T runs on the same MFMA with V in fp6 and P in fp8 (u in
+//     [0, 15] is exact in e4m3, and a step's sums are integers below 2^24),
+//     so each step's PV is exact; it accumulates across steps in fp32
+//     registers, scaled by beta only when a query's running max rises (rare
+//     after the first few steps).  The row sum of the codes is one more MFMA
+//     per step (16x16x128, the same P operand against an fp4 0/1 selector),
+//     so it costs no VALU work and lands in every lane that owns the query.
 #include <type_traits>
 
 #include "ra_common.h"
@@ -56,17 +55,8 @@ struct Cfg {
   static constexpr int QC = D / 64;        // 64-channel chunks of the Q.K contraction
   static constexpr int DT = D / 32;        // 32-channel tiles of O
   static constexpr int KT = qk6_tile_bytes(D);   // fp6 K tile of 64 keys (48 D bytes)
-  static constexpr int VT = D * 64;        // fp8 V tile: D rows of 64 slots
+  static constexpr int VT = v6_tile_bytes(D);   // fp6 V tile of 64 keys (48 D bytes)
 };
-
-// V rows (64 bytes) are XOR-swizzled in 16-byte chunks in LDS.  The gfx950
-// LDS serves a ds_read_b128 in groups of 16 lanes over 64 banks (256 B); the
-// operand reads of one group touch 16 consecutive rows at one logical chunk,
-// so row mod 4 picks the quarter of the bank window and the XOR the slot
-// within it, giving the 16 rows 16 distinct 16-byte slots.
-__device__ __forceinline__ int swz64(int row, int chunk) {
-  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
 
 template <int D>
 struct State {
@@ -160,12 +150,10 @@ __device__ __forceinline__ v4i make_rsrc(const uint8_t* base, uint32_t bytes) {
 
 __device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Copies of one step's K tile (fp6, 48 D bytes) and V tile (D rows x 64
-// slot bytes) by NW waves.  The tiles are cut into 16-byte slots numbered in
-// LDS order; a wave copies 64 consecutive slots per instruction, K slots
-// first.  K slots are copied in place; V slot (row r, physical chunk cp)
-// holds logical chunk cp ^ swizzle(r), so the source address carries the
-// swizzle.
+// Copies of one step's K tile and V tile (fp6, 48 D bytes each) by NW
+// waves.  The tiles are cut into 16-byte slots numbered in LDS order; a wave
+// copies 64 consecutive slots per instruction, K slots first.  Both tiles
+// are copied as they lie.
 template <int D, int NW>
 struct TileDma {
   static constexpr int KS = Cfg<D>::KT / 16;
@@ -192,12 +180,11 @@ struct TileDma {
       } else if (first < KS) {
         kind[j] = 1;
         lds[j] = first * 16;
-        off[j] = (first + lane) * 16;          // the fp6 K tile is copied as it lies
+        off[j] = (first + lane) * 16;
       } else {
-        const int s = first - KS + lane, r = s >> 2, cp = s & 3;
         kind[j] = 2;
         lds[j] = (first - KS) * 16;
-        off[j] = r * 64 + ((cp ^ ((r >> 2) & 3)) * 16);
+        off[j] = (first - KS + lane) * 16;
       }
       kind[j] = __builtin_amdgcn_readfirstlane(kind[j]);
       lds[j] = __builtin_amdgcn_readfirstlane(lds[j]);
@@ -359,24 +346,24 @@ __device__ __forceinline__ void lsum_step(const v8i& sel, const uint32_t (&p)[2]
   lsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb, lsum, 4, 0, 0, 0, 0, 0);
 }
 
-// O^T += V^T P^T over the 64 keys of the step: lane half hf supplies slots
-// 32hf..32hf+31, i.e. 16-byte chunks 2hf and 2hf+1 of each V row.  Rows
-// 32 dt + ln carry the swizzle of row ln (32 is a multiple of 16), so tile
-// dt lies 2048 dt bytes past the two lane bases.
+// O^T += V^T P^T over the 64 keys of the step on the f8f6f4 MFMA with an
+// fp6 A operand (V, cbsz 2) and an fp8 B operand (P).  Lane (ln, hf)
+// supplies the fp6 string of channel 32 dt + ln, half hf: one 16-byte and
+// one 8-byte read, tile dt 512 and 256 bytes past the lane bases.
 template <int D>
 __device__ __forceinline__ void pv_step(const uint8_t* vst, const uint32_t (&p)[2][4],
                                         v16f (&acc)[Cfg<D>::DT]) {
   const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const v8i pb = v8i{(int)p[0][0], (int)p[0][1], (int)p[0][2], (int)p[0][3],
                      (int)p[1][0], (int)p[1][1], (int)p[1][2], (int)p[1][3]};
-  lds_cu8* const v0p = lds_base(vst + swz64(ln, 2 * hf));
-  lds_cu8* const v1p = lds_base(vst + swz64(ln, 2 * hf + 1));
+  lds_cu8* const vlo = lds_base(vst + v6_lo_off(D, ln, hf));
+  lds_cu8* const vhi = lds_base(vst + v6_hi_off(D, ln, hf));
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
-    const v4i v0 = lds_ld<v4i>(v0p + 2048 * dt);
-    const v4i v1 = lds_ld<v4i>(v1p + 2048 * dt);
-    const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-    acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[dt], 0, 0, 0, 0, 0, 0);
+    const v4i lo = lds_ld<v4i>(vlo + 512 * dt);
+    const v2i hi = lds_ld<v2i>(vhi + 256 * dt);
+    const v8i va = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+    acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[dt], 2, 0, 0, 0, 0, 0);
   }
 }
 

@@ -367,8 +367,8 @@ __global__ void k_zero_u32(uint32_t* p, size_t n) {
 }
 
 // V quantization + transpose into the PV operand layout: one workgroup per
-// (64-key block, b*h); each thread writes (channel, 16-slot group) units of
-// 16 e4m3 bytes.
+// (64-key block, b*h); thread (d, hf) packs the 32 codes lane half hf of
+// the PV MFMA supplies for channel d into one fp6 string (v6_* layout).
 template <bool BF16, int D, bool VH>
 __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
   constexpr int PER = D / 4;
@@ -389,28 +389,27 @@ __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
   for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = tmp[e];
   __syncthreads();
 
-  constexpr int UNITS = D * 4 / 256;       // (channel, 16-slot group) units per thread
-#pragma unroll
-  for (int uu = 0; uu < UNITS; ++uu) {
-    const int unit = t * UNITS + uu;
-    const int d = unit >> 2, sg = unit & 3;
+  if (t < 2 * D) {
+    const int d = t >> 1, hf = t & 1;
     const float amax = __uint_as_float(a.vamax[(size_t)bh * D + d]);
     const float inv = 7.0f / amax;
-    uint32_t w[4];
+    uint32_t cw[8];                    // the 32 codes, one e2m3 code per byte
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
+    for (int q4 = 0; q4 < 8; ++q4) {
       uint32_t acc = 0;
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
-        const int key = slot_key_pv(sg * 16 + 4 * q4 + bi);
+        const int key = slot_key_pv(v6_slot(hf, 4 * q4 + bi));
         const int c = amax > 0.0f ? quant_code(tile[key][d], inv) : 0;
-        acc |= e4m3_of_code(c) << (8 * bi);
+        acc |= e2m3_of_code(c) << (8 * bi);
       }
-      w[q4] = acc;
+      cw[q4] = acc;
     }
-    uint8_t* dst = a.v_out + (((size_t)bh * a.nkb + kb) * D + d) * 64 + sg * 16;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    if (kb == 0 && sg == 0) a.s_v[(size_t)bh * D + d] = amax > 0.0f ? amax / 7.0f : 0.0f;
+    uint8_t* dst = a.v_out + ((size_t)bh * a.nkb + kb) * v6_tile_bytes(D);
+    *reinterpret_cast<uint4*>(dst + v6_lo_off(D, d, hf)) =
+        make_uint4(fp6_word<0>(cw), fp6_word<1>(cw), fp6_word<2>(cw), fp6_word<3>(cw));
+    *reinterpret_cast<uint2*>(dst + v6_hi_off(D, d, hf)) = make_uint2(fp6_word<4>(cw), fp6_word<5>(cw));
+    if (kb == 0 && hf == 0) a.s_v[(size_t)bh * D + d] = amax > 0.0f ? amax / 7.0f : 0.0f;
   }
 }
 

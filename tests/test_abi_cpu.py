@@ -93,7 +93,7 @@ def test_workspace_sizes(L):
     from bit_quantized_attention_rope3d_amd.api import Plan
     p = Plan(1, 40, 128, (21, 45, 80), (44, 42, 42), rot="half")
     Npad = 1182 * 64
-    codes = 40 * Npad * 128 * 3 // 4 * 2 + 40 * Npad * 128   # Q, K: 6 bits per code; V: one byte
+    codes = 40 * Npad * 128 * 3 // 4 * 3                      # Q, K, V: 6 bits per code
     assert p.workspace_bytes >= codes + 2 * 40 * 1182 * 4 + 2 * 40 * 128 * 4
     assert p.workspace_bytes < codes + 2 * 1024 * 1024
     b = Plan(1, 40, 128, (21, 45, 80), (44, 42, 42), prec="bf16")
