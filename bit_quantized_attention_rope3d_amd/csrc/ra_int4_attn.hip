@@ -241,6 +241,11 @@ template <typename T>
 __device__ __forceinline__ T lds_ld(lds_cu8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
 }
+// Compiler-only fence after the reads of one fp6 operand: otherwise the
+// 8-byte reads of two operands are merged into one ds_read2_b64, whose
+// result then has to be moved next to each operand's 16-byte part (the six
+// registers of an fp6 operand must be consecutive).  No instruction.
+__device__ __forceinline__ void operand_fence() { asm volatile("" ::: "memory"); }
 
 // ---- building blocks of one 64-key step for the 32 queries of a wave ------
 
@@ -263,6 +268,7 @@ __device__ __forceinline__ void qk_step(const uint8_t* kst, const v8i (&qop)[Cfg
       const int rg = 128 * qc + 32 * mt;   // (64 g + row) - (64 hf + ln)
       const v4i lo = lds_ld<v4i>(klo + 16 * rg);
       const v2i hi = lds_ld<v2i>(khi + 8 * rg);
+      operand_fence();
       const v8i ka = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
       s[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qop[qc], s[mt], 2, 2, 0, 0, 0, 0);
     }
@@ -362,6 +368,7 @@ __device__ __forceinline__ void pv_step(const uint8_t* vst, const uint32_t (&p)[
   for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
     const v4i lo = lds_ld<v4i>(vlo + 512 * dt);
     const v2i hi = lds_ld<v2i>(vhi + 256 * dt);
+    operand_fence();
     const v8i va = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
     acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[dt], 2, 0, 0, 0, 0, 0);
   }
