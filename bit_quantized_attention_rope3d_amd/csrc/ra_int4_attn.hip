@@ -16,7 +16,7 @@
 //   * Per 64-key step the K and V code tiles (6 KB of fp6 each for D = 128)
 //     are copied from global memory straight into LDS by buffer loads with
 //     the LDS-direct bit (16 bytes per lane, no VGPRs, no VALU), as they lie.
-//     Eight stages of each; the workgroup barrier is taken once every four
+//     Ten stages of each; the workgroup barrier is taken once every five
 //     steps.
 //   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 with both operands fp6 e2m3
 //     (exact for |code| <= 7, and twice the fp8 rate); every partial sum is
@@ -47,7 +47,7 @@ namespace ra {
 
 constexpr int kWaves = 12;                 // waves per workgroup
 constexpr int kQTile = 32 * kWaves;        // query rows per workgroup
-constexpr int kSync = 4;                   // steps per workgroup barrier
+constexpr int kSync = 5;                   // steps per workgroup barrier
 constexpr int kStages = 2 * kSync;         // LDS stages of K and of V tiles
 
 template <int D>
