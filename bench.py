@@ -51,6 +51,8 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip the sustained MFMA throughput probe")
     ap.add_argument("--main-only-steps", type=int, default=0,
                     help="extra launches of the attention kernel alone (profiling)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -117,6 +119,29 @@ def time_steps(fn, steps, stream):
         mid.append(b.elapsed_time(c))
     total = evs[0][0].elapsed_time(evs[-1][2])
     return total, first, mid, wall
+
+
+PUBLISHED_PEAKS = {"i8": INT8_PEAK_TOPS, "fp8": FP8_PEAK_TFLOPS, "fp6": FP6_PEAK_TFLOPS,
+                   "fp6_fp8": FP8_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS}
+
+
+def sustained_mfma(achieved_main):
+    """Throughput of back-to-back independent MFMAs of each operand type on
+    every SIMD (3 waves each), with the engine clock over the launch: the
+    rates the chip sustains under a pure matrix-core load, next to the
+    published 2.4 GHz peaks.  The INT4 kernel's QK^T is fp6 x fp6 and its PV
+    fp6 x fp8, half the operations each."""
+    from bit_quantized_attention_rope3d_amd.api import mfma_peak
+    out = {}
+    for kind, peak in PUBLISHED_PEAKS.items():
+        t, ghz = mfma_peak(kind)
+        out[kind] = dict(tops=t, clock_ghz=ghz, frac_of_published=t / peak)
+    blend = 2.0 / (1.0 / out["fp6"]["tops"] + 1.0 / out["fp6_fp8"]["tops"])
+    out["int4_kernel_blend_tops"] = blend
+    out["int4_main_frac_of_sustained_blend"] = achieved_main / blend
+    out["note"] = ("T ops/s of 768 workgroups x 4 waves, each wave issuing 4 independent MFMA chains "
+                   "(32x32 shapes); clock = shader cycles / 100 MHz real-time ticks of one wave")
+    return out
 
 
 def cpu_baseline(w, q, k, v, gpu_out, target_s):
@@ -216,6 +241,11 @@ def main():
     pro_avg = float(np.mean(pro_ms))
     achieved_main = ops / (main_avg * 1e-3) / 1e12
 
+    sustained = None
+    if not args.no_peak_probe:
+        log("sustained MFMA probe")
+        sustained = sustained_mfma(achieved_main)
+
     res_bf16 = None
     if not args.no_bf16:
         pb = Plan(w.batch, w.heads, w.head_dim, w.grid, w.seg, rot=w.rot, prec="bf16",
@@ -280,6 +310,7 @@ def main():
         "speedup_vs_bf16": (res_bf16["ms_per_step"] / ms4) if res_bf16 else None,
         "wall_s_timed_int4": wall4,
         "roofline": roof,
+        "sustained_mfma": sustained,
         "cpu_baseline": None,
     }
 

@@ -193,3 +193,33 @@ def copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int | None = None, stream
 
 def pgrid() -> int:
     return int(lib().ra_pgrid())
+
+
+PEAK_KINDS = {"i8": 0, "fp8": 1, "fp6": 2, "fp6_fp8": 3, "bf16": 4}
+
+
+def mfma_peak(kind: str, iters: int = 20000, blocks: int = 768, stream=None):
+    """Sustained matrix-core throughput of one operand type through
+    ra_bench_mfma_peak: returns (T ops/s, engine clock in GHz over the launch).
+    768 workgroups of 4 waves put 3 waves on each SIMD of the 256 CUs."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    clk = torch.zeros(4, dtype=torch.int64, device=dev)
+    ops = ctypes.c_double()
+    st = _stream_ptr(stream, dev)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+
+    def launch():
+        check(lib().ra_bench_mfma_peak(PEAK_KINDS[kind], int(iters), int(blocks), _ptr(sink), _ptr(clk),
+                                       ctypes.byref(ops), st), "ra_bench_mfma_peak")
+
+    launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    launch()
+    e1.record(s)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1)
+    c = clk.cpu().tolist()
+    ghz = (c[1] - c[0]) / max(1, c[3] - c[2]) * 0.1
+    return ops.value / (ms * 1e-3) / 1e12, ghz

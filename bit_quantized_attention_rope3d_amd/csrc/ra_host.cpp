@@ -579,4 +579,16 @@ ra_status ra_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) 
   return st == RA_OK ? ok() : st;
 }
 
+ra_status ra_bench_mfma_peak(int32_t kind, int32_t iters, int32_t blocks, float* sink, uint64_t* clk,
+                             double* ops_out, hipStream_t stream) {
+  const int per = ra::mfma_peak_ops_per_instr(kind);
+  if (per == 0) return fail(RA_ERR_INVALID_ARG, "unknown MFMA kind %d", kind);
+  if (iters < 1 || blocks < 1) return fail(RA_ERR_INVALID_ARG, "iters and blocks must be >= 1");
+  if (!sink || !clk || !ops_out) return fail(RA_ERR_INVALID_ARG, "null argument");
+  *ops_out = (double)per * ra::mfma_peak_chains() * iters * 4.0 * blocks;
+  ra::launch_mfma_peak(kind, iters, blocks, sink, clk, stream);
+  ra_status st = after_launch("mfma peak");
+  return st == RA_OK ? ok() : st;
+}
+
 }  // extern "C"

@@ -27,7 +27,7 @@ struct VAmaxArgs {
 struct VQuantArgs {
   const void* v;
   const uint32_t* vamax;
-  uint8_t* v_out;     // int4: [B*H, nkb, D, 64] e4m3 code bytes; bf16: [B*H, nkb, D, 64] bf16
+  uint8_t* v_out;     // int4: [B*H, nkb] 64-key fp6 e2m3 tiles (48 D bytes each); bf16: [B*H, nkb, D, 64] bf16
   float* s_v;         // [B*H, D]
   int N, H, nkb;
 };
@@ -64,5 +64,11 @@ void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipS
 void launch_pmap_probe(const float* x, uint8_t* u, int64_t n, int p_mode, hipStream_t st);
 void launch_bf16_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
 void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+
+// Operand types of the matrix-core throughput kernel (ra_peak.hip).
+enum PeakKind { kPeakI8 = 0, kPeakFp8 = 1, kPeakFp6 = 2, kPeakFp6Fp8 = 3, kPeakBf16 = 4 };
+void launch_mfma_peak(int kind, int iters, int blocks, float* sink, uint64_t* clk, hipStream_t st);
+int mfma_peak_ops_per_instr(int kind);   // 0 for an unknown kind
+int mfma_peak_chains();                  // independent MFMAs per wave per iteration
 
 }  // namespace ra

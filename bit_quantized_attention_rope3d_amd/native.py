@@ -70,6 +70,7 @@ _SIGS = {
     "ra_debug_pmap": (c_i32, [c_void, c_void, c_i64, c_i32, c_void]),
     "ra_debug_tables": (c_i32, [c_void, c_i32, c_void, c_void]),
     "ra_copy": (c_i32, [c_void, c_void, c_size, c_void]),
+    "ra_bench_mfma_peak": (c_i32, [c_i32, c_i32, c_i32, c_void, c_void, ctypes.POINTER(ctypes.c_double), c_void]),
 }
 
 _lib = None

@@ -199,6 +199,21 @@ ra_status ra_debug_tables(ra_plan plan, int32_t seg, float* cos_out, float* sin_
 /* Plain device-to-device copy kernel (bandwidth reference).  Enqueue only. */
 ra_status ra_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
+/* Matrix-core throughput probe: a measurement helper beside the attention
+ * path, used to state the sustained MFMA rate and the engine clock it is
+ * reached at next to the published peaks.  kind: 0 INT8 (32x32x32 i8),
+ * 1 fp8 x fp8, 2 fp6 x fp6, 3 fp6 A x fp8 B (32x32x64 f8f6f4), 4 bf16
+ * (32x32x16).  Launches `blocks` workgroups of 4 waves; each wave issues
+ * iters x 4 independent MFMAs of that kind.  clk (device, 4 x uint64_t)
+ * receives, from wave 0 of workgroup 0, the shader cycle counter at its
+ * start and end, then the 100 MHz real-time counter at its start and end.
+ * sink (device, 1 float) keeps the results live and is not written for
+ * these operands.  *ops_out (host) receives the operations of one launch
+ * (2 per multiply-add).  Unknown kind, iters < 1 or blocks < 1 return
+ * RA_ERR_INVALID_ARG.  Enqueue only. */
+ra_status ra_bench_mfma_peak(int32_t kind, int32_t iters, int32_t blocks, float* sink, uint64_t* clk,
+                             double* ops_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

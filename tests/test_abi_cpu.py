@@ -167,3 +167,13 @@ def test_schedule_agrees_with_oracle(L, ora):
 
 def test_pgrid_agrees_with_oracle(L, ora):
     assert native.lib().ra_pgrid() == ora.pgrid()
+
+
+def test_mfma_peak_probe_validates_before_launch(L):
+    a = ctypes.c_void_p(0x10000)
+    ops = ctypes.c_double()
+    probe = L.ra_bench_mfma_peak
+    assert native.STATUS[probe(99, 10, 10, a, a, ctypes.byref(ops), None)] == "RA_ERR_INVALID_ARG"
+    assert native.STATUS[probe(0, 0, 10, a, a, ctypes.byref(ops), None)] == "RA_ERR_INVALID_ARG"
+    assert native.STATUS[probe(0, 10, 0, a, a, ctypes.byref(ops), None)] == "RA_ERR_INVALID_ARG"
+    assert native.STATUS[probe(0, 10, 10, None, a, ctypes.byref(ops), None)] == "RA_ERR_INVALID_ARG"

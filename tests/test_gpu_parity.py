@@ -330,3 +330,13 @@ def test_full_rotation_matches_oracle(ora, case):
     say("full rotation %s: max|gpu-oracle| %.2e cos %.7f | vs fp64 mean %.3e"
         % (case, err, cos, np.abs(o - ref).mean()))
     assert err <= 2e-3 and cos >= 0.999
+
+
+def test_mfma_peak_probe():
+    """The throughput probe runs for every operand type and reports a
+    plausible engine clock and a positive rate."""
+    from bit_quantized_attention_rope3d_amd.api import PEAK_KINDS, mfma_peak
+    for kind in PEAK_KINDS:
+        t, ghz = mfma_peak(kind, iters=2000)
+        say("mfma probe %s: %.0f T ops/s at %.3f GHz" % (kind, t, ghz))
+        assert t > 0 and 0.5 < ghz < 3.5
