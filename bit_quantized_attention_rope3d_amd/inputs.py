@@ -145,3 +145,39 @@ def small(name="small", heads=3, head_dim=128, grid=(3, 5, 7), seg=None, rot="ha
 def schedule_seed(step: int, block: int, n_blocks: int = 40) -> int:
     """Seed of the fresh tensors of one call in the step x block sweep."""
     return 1000 + step * n_blocks + block
+
+
+def generate_device(w: Workload, seed: int, device="cuda"):
+    """Fresh Q, K, V [B, N, H, D] drawn on the device, for sweeps that need a
+    new full-size tensor per call (drawing 75,600 x 40 x 128 normals on the
+    host takes seconds).  Normals come from torch's Philox generator seeded
+    with `seed`; the outlier channels and multipliers are drawn on the host
+    from the same seed, as in generate().  Returns tensors of the workload's
+    dtype (bf16 or float32)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    B, N, H, D = w.batch, w.tokens, w.heads, w.head_dim
+    shape = (B, N, H, D)
+    mult = np.ones((H, D), np.float32)
+    heavy = []
+    for h, sel in enumerate(outlier_channels(w, np.random.default_rng(seed))):
+        for c, m in sel:
+            mult[h, c] = m
+            heavy.append((h, c))
+    mult_d = torch.from_numpy(mult).to(device)
+    out = []
+    for _ in range(3):
+        out.append(torch.randn(shape, generator=g, device=device, dtype=torch.float32))
+    q, k, v = out
+    if w.outlier_dist == "student_t3":
+        # t(3) = z / sqrt(chi2_3 / 3) on the outlier channels of Q and K.
+        for x in (q, k):
+            for h, c in heavy:
+                z = torch.randn((B, N), generator=g, device=device)
+                chi = torch.randn((3, B, N), generator=g, device=device).square().sum(0)
+                x[:, :, h, c] = z / torch.sqrt(chi / 3.0)
+    q.mul_(mult_d)
+    k.mul_(mult_d)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return q.to(dt), k.to(dt), v.to(dt)
