@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan720")
+    ap.add_argument("--inputs", default="recipe", choices=["recipe", "plain", "mild", "student_t3"],
+                    help="outlier recipe of the synthetic inputs: the workload's own (default), none, "
+                         "x U[3,5] instead of x U[10,30], or Student-t(3) channels in the height/width segments")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -203,7 +206,7 @@ def main():
     from bit_quantized_attention_rope3d_amd import inputs
     from bit_quantized_attention_rope3d_amd.api import Plan
 
-    w = inputs.get(args.workload)
+    w = inputs.with_inputs(inputs.get(args.workload), args.inputs)
     log("generating %s inputs (seed %d)" % (w.name, w.seed))
     q, k, v, info = inputs.generate(w)
 
@@ -301,7 +304,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "grid": list(w.grid), "tokens": w.tokens, "seg": list(w.seg), "rot": w.rot,
-                   "in_dtype": "bf16", "out_dtype": "f32", "seed": w.seed},
+                   "in_dtype": "bf16", "out_dtype": "f32", "seed": w.seed,
+                   "inputs": args.inputs},
         "pct_int8_peak": 100.0 * tops / INT8_PEAK_TOPS,
         "int4_main_ms": main_avg,
         "int4_prologue_ms": pro_avg,

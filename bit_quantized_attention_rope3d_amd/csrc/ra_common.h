@@ -82,12 +82,6 @@ __host__ __device__ constexpr int slot_key_bf16(int slot) {
          4 * ((slot >> 3) & 1) + (slot & 3);
 }
 
-// OCP fp8 e4m3 byte of an integer code c in [-7, 7] (exact): sign in bit 7,
-// |c| = 0..7 -> 00 38 40 44 48 4A 4C 4E.
-__host__ __device__ constexpr uint32_t e4m3_of_code(int c) {
-  return (c < 0 ? 0x80u : 0u) | (uint32_t)((0x4E4C4A4844403800ull >> (8 * (c < 0 ? -c : c))) & 0xFFu);
-}
-
 // OCP fp6 e2m3 code (bits 0..5) of an integer c in [-7, 7] (exact): sign in
 // bit 5, |c| = 0..7 -> 00 08 10 14 18 1A 1C 1E.
 __host__ __device__ constexpr uint32_t e2m3_of_code(int c) {
@@ -107,10 +101,6 @@ __device__ __forceinline__ uint32_t pmap_insert(float x, uint32_t sel, uint32_t 
   return __builtin_amdgcn_cvt_pk_u8_f32(y, sel, acc);
 }
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
-  return __uint_as_float(((uint32_t)b) << 16);
-}
-
 // Round-to-nearest-even float -> bf16 bits (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -122,10 +112,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // same query columns).  v_permlane32_swap returns, per lane, its own value in
 // one result and its partner's in the other, so a symmetric op of both
 // results is the cross-half reduction whichever half the lane is in.
-__device__ __forceinline__ int xhalf_max_i(int x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return max((int)r[0], (int)r[1]);
-}
 __device__ __forceinline__ float xhalf_max_f(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));

@@ -83,6 +83,22 @@ def get(name: str) -> Workload:
     return WORKLOADS[name]
 
 
+def with_inputs(w: Workload, recipe: str) -> Workload:
+    """The workload with another outlier recipe: 'recipe' (its own), 'plain'
+    (no outlier channels), 'mild' (multipliers U[3, 5] instead of
+    U[10, 30]) or 'student_t3' (heavy-tailed channels in the height and width
+    segments, as in the HunyuanVideo-like workload)."""
+    if recipe == "recipe":
+        return w
+    if recipe == "plain":
+        return w.with_(outliers_per_segment=(0, 0, 0))
+    if recipe == "mild":
+        return w.with_(outlier_scale=(3.0, 5.0))
+    if recipe == "student_t3":
+        return w.with_(outlier_segments=(1, 2), outliers_per_segment=(0, 1, 2), outlier_dist="student_t3")
+    raise ValueError("unknown input recipe %r" % recipe)
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even float32 -> bfloat16 bit patterns (uint16)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)

@@ -58,9 +58,9 @@ def _metrics(o, ref):
 
 def _workload(name):
     if name == "wan720_plain":
-        return inputs.get("wan720").with_(name=name, outliers_per_segment=(0, 0, 0))
+        return inputs.with_inputs(inputs.get("wan720"), "plain").with_(name=name)
     if name == "wan720_mild":
-        return inputs.get("wan720").with_(name=name, outlier_scale=(3.0, 5.0))
+        return inputs.with_inputs(inputs.get("wan720"), "mild").with_(name=name)
     return inputs.get(name)
 
 
