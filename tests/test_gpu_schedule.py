@@ -140,6 +140,10 @@ def test_schedule_sweep_small(ora):
                     reason="full-size sweep (400 calls at 75,600 tokens) runs with RA_FULL_SWEEP=1")
 def test_schedule_sweep_wan720(ora):
     w = inputs.get("wan720")
-    ora.set_threads(2)
-    s = run_sweep(ora, w, 10, 40, (2, 2, 4, 4), rows_per_call=64, all_heads=False, workers=8)
+    threads = ora.get_threads()
+    ora.set_threads(2)      # eight checking threads share the host cores
+    try:
+        s = run_sweep(ora, w, 10, 40, (2, 2, 4, 4), rows_per_call=64, all_heads=False, workers=8)
+    finally:
+        ora.set_threads(threads)
     assert s["calls"] == 400 and s["int4_calls"] == 192
