@@ -308,6 +308,10 @@ def main():
                    "inputs": args.inputs},
         "pct_int8_peak": 100.0 * tops / INT8_PEAK_TOPS,
         "int4_main_ms": main_avg,
+        "step_ms_median": float(np.median(np.add(pro_ms, main_ms))),
+        "step_ms_min": float(np.min(np.add(pro_ms, main_ms))),
+        "int4_main_ms_median": float(np.median(main_ms)),
+        "int4_main_ms_min": float(np.min(main_ms)),
         "int4_prologue_ms": pro_avg,
         "prologue_gbs": pro_bytes / (pro_avg * 1e-3) / 1e9,
         "bf16_fallback": res_bf16,
