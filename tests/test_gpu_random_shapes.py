@@ -1,0 +1,59 @@
+"""Seeded random configurations through the C ABI against the oracle.
+
+Each case draws batch, heads, head dim (64 or 128), a 3D grid (ragged token
+counts), a valid frame/height/width split of the head dim (even, positive
+segments), the rotation (none, Interleaved, Half, full Walsh-Hadamard), the
+input dtype, the P mode and the V-side Hadamard, then checks every Q/K/V
+code and scale bit for bit against the oracle's prologue and the output
+against the oracle's binary64 float path (max-abs 2e-3, cosine 0.999).
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_attention_rope3d_amd import inputs
+
+from gpu_helpers import cosine, dev, plan_for, say
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+ROTS = ["none", "interleaved", "half", "full"]
+
+
+def random_case(seed):
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([64, 128]))
+    s0 = 2 * int(rng.integers(1, D // 2 - 1))
+    s1 = 2 * int(rng.integers(1, (D - s0) // 2))
+    seg = (s0, s1, D - s0 - s1)
+    grid = tuple(int(x) for x in rng.integers(1, 7, size=3))
+    w = inputs.Workload("rand%d" % seed, int(rng.integers(1, 3)), int(rng.integers(1, 4)), D, grid, seg,
+                        rot=ROTS[int(rng.integers(0, 4))], dtype=str(rng.choice(["bf16", "f32"])),
+                        seed=100 + seed, outliers_per_segment=(1, 1, 1))
+    return w, int(rng.integers(0, 2)), int(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configuration(ora, seed):
+    w, p_mode, vh = random_case(seed)
+    say("random %d: B%d H%d D%d grid %s seg %s rot %s %s p_mode %d v_hadamard %d"
+        % (seed, w.batch, w.heads, w.head_dim, w.grid, w.seg, w.rot, w.dtype, p_mode, vh))
+    assert all(s > 0 and s % 2 == 0 for s in w.seg) and sum(w.seg) == w.head_dim
+    q, k, v, _ = inputs.generate(w)
+    p = plan_for(w, p_mode=p_mode, v_hadamard=vh)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    ws = p.workspace()
+    got = p.debug_prologue(qd, kd, vd, ws)
+    pro = ora.prologue(q, k, v, w.grid, w.seg, w.theta, w.rot_id, v_hadamard=bool(vh))
+    for key in ("q_codes", "k_codes", "v_codes"):
+        assert np.array_equal(got[key], pro[key]), key
+    for key in ("s_q", "s_k", "s_v"):
+        assert np.array_equal(got[key].view(np.uint32), pro[key].view(np.uint32)), key
+    o = p.forward(qd, kd, vd, workspace=ws).cpu().numpy()
+    want = ora.attention_full(pro, p_mode=p_mode, v_hadamard=bool(vh))
+    err, cos = float(np.abs(o - want).max()), cosine(o, want)
+    say("random %d: max|gpu-oracle| %.2e cos %.8f" % (seed, err, cos))
+    assert err <= 2e-3 and cos >= 0.999
