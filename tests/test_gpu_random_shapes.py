@@ -1,4 +1,5 @@
-"""Seeded random configurations through the C ABI against the oracle.
+"""Seeded random configurations through the C ABI against the oracle (and, for
+the bf16 fallback, against fp64 attention of its own rounded inputs).
 
 Each case draws batch, heads, head dim (64 or 128), a 3D grid (ragged token
 counts), a valid frame/height/width split of the head dim (even, positive
@@ -57,3 +58,22 @@ def test_random_configuration(ora, seed):
     err, cos = float(np.abs(o - want).max()), cosine(o, want)
     say("random %d: max|gpu-oracle| %.2e cos %.8f" % (seed, err, cos))
     assert err <= 2e-3 and cos >= 0.999
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_configuration_bf16_path(ora, seed):
+    """The bf16 fallback on the same random shapes, against fp64 attention of
+    its own bf16-rounded RoPE'd Q/K and bf16 V (the bf16 path's bar)."""
+    from oracle import ref_fp64
+    from gpu_helpers import bf16_round
+    w, _, _ = random_case(1000 + seed)
+    say("random bf16 %d: B%d H%d D%d grid %s seg %s %s" % (seed, w.batch, w.heads, w.head_dim, w.grid, w.seg, w.dtype))
+    q, k, v, _ = inputs.generate(w)
+    o = plan_for(w, prec="bf16").forward(dev(q), dev(k), dev(v)).cpu().numpy()
+    qf, kf, vf = ora.as_f32(q), ora.as_f32(k), ora.as_f32(v)
+    qr = bf16_round(ref_fp64.rope3d(qf, w.grid, w.seg, w.theta).astype(np.float32))
+    kr = bf16_round(ref_fp64.rope3d(kf, w.grid, w.seg, w.theta).astype(np.float32))
+    ref = ref_fp64.attention(qr, kr, bf16_round(vf))
+    err, cos = float(np.abs(o - ref).max()), cosine(o, ref)
+    say("random bf16 %d: max %.2e cos %.8f" % (seed, err, cos))
+    assert err <= 2e-2 and cos >= 0.9999
