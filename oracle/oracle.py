@@ -24,15 +24,19 @@ BLOCK = 64
 
 __all__ = [
     "build", "lib", "ROT_NONE", "ROT_INTERLEAVED", "ROT_HALF", "ROT_FULL", "ROT_NAMES",
-    "BLOCK", "pgrid", "bf16_bits_to_f32", "as_f32", "rope_table", "rope_rotate",
+    "BLOCK", "bf16_bits_to_f32", "as_f32", "rope_table", "rope_rotate",
     "quant_qk", "quant_v", "fwht", "prologue", "pmap_thresholds", "pmap", "P_SCALE", "P_ZERO",
-    "attention_rows", "attention_tile", "attention_full", "schedule_full_precision",
+    "attention_rows", "attention_tile", "attention_full", "code_digests", "schedule_full_precision",
     "set_threads", "get_threads",
 ]
 
 
 def build(force: bool = False) -> str:
-    """Compile ra_oracle.c into libra_oracle.so next to it."""
+    """Compile ra_oracle.c into libra_oracle.so next to it.  With
+    ORA_LIB_PATH set, that prebuilt variant is used instead (tests that plant
+    a mistake in a copy of the oracle point the suite at it)."""
+    if os.environ.get("ORA_LIB_PATH"):
+        return os.environ["ORA_LIB_PATH"]
     if force or not os.path.exists(_LIB_PATH) or (
             os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
@@ -47,11 +51,9 @@ def lib():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            L = ctypes.CDLL(_LIB_PATH)
+            L = ctypes.CDLL(build())
             P = ctypes.c_void_p
             i32, f64 = ctypes.c_int, ctypes.c_double
-            L.ora_pgrid.restype = i32
             L.ora_block.restype = i32
             L.ora_set_threads.argtypes = [i32]
             L.ora_get_threads.restype = i32
@@ -59,18 +61,17 @@ def lib():
             L.ora_rope_rotate.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, f64, i32]
             L.ora_quant_qk.argtypes = [P, i32, i32, i32, i32, P, P]
             L.ora_quant_v.argtypes = [P, i32, i32, i32, i32, P, P]
-            L.ora_pmap_thresholds.argtypes = [i32, P]
-            L.ora_pmap.argtypes = [P, ctypes.c_int64, P]
-            L.ora_pmap_thresholds_p.argtypes = [i32, i32, P]
+            L.ora_pmap_thresholds_p.argtypes = [i32, P]
             L.ora_pmap_p.argtypes = [P, ctypes.c_int64, i32, P]
             L.ora_fwht_rows.argtypes = [P, ctypes.c_int64, i32]
             L.ora_attention_head.argtypes = [P, P, P, P, P, P, i32, i32, f64, i32, i32,
-                                             P, i32, P, P, i32, P, P, P, P]
+                                             P, i32, P, P, i32, P, P, P, P, P]
+            L.ora_code_digests.argtypes = [P, P, P, P, i32, i32, f64, i32, P, i32, P, P, P]
             L.ora_schedule_full_precision.argtypes = [i32] * 8
             for name in ("ora_rope_table", "ora_rope_rotate", "ora_quant_qk",
-                         "ora_quant_v", "ora_pmap_thresholds", "ora_pmap",
-                         "ora_pmap_thresholds_p", "ora_pmap_p", "ora_fwht_rows",
-                         "ora_attention_head", "ora_schedule_full_precision"):
+                         "ora_quant_v", "ora_pmap_thresholds_p", "ora_pmap_p", "ora_fwht_rows",
+                         "ora_attention_head", "ora_code_digests",
+                         "ora_schedule_full_precision"):
                 getattr(L, name).restype = i32
             _lib = L
     return _lib
@@ -83,11 +84,6 @@ def _p(a):
 def _check(rc, what):
     if rc != 0:
         raise ValueError("oracle %s rejected its arguments (rc=%d)" % (what, rc))
-
-
-def pgrid() -> int:
-    """Steps per log2 unit of the grid on which the P exponent is rounded."""
-    return lib().ora_pgrid()
 
 
 def set_threads(n: int) -> None:
@@ -176,17 +172,18 @@ P_SCALE = {0: 15, 1: 7}        # p_mode 0: range-optimized; 1: symmetric
 P_ZERO = {0: 8, 1: 0}          # zero-point: code = u - P_ZERO[p_mode]
 
 
-def pmap_thresholds(G: int | None = None, p_mode: int = 0) -> np.ndarray:
-    tau = np.empty(P_SCALE[p_mode], np.int32)
-    _check(lib().ora_pmap_thresholds_p(int(G or pgrid()), int(p_mode), _p(tau)), "pmap_thresholds")
-    return tau
+def pmap_thresholds(p_mode: int = 0) -> np.ndarray:
+    """T_k (binary32): the smallest d with P * 2^d >= k + 1/2, k = 0..P-1."""
+    T = np.empty(P_SCALE[p_mode], np.float32)
+    _check(lib().ora_pmap_thresholds_p(int(p_mode), _p(T)), "pmap_thresholds")
+    return T
 
 
-def pmap(x, p_mode: int = 0) -> np.ndarray:
-    """u = code + zero-point for grid exponents x (binary32 values)."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = np.empty(x.shape, np.uint8)
-    _check(lib().ora_pmap_p(_p(x), x.size, int(p_mode), _p(u)), "pmap")
+def pmap(d, p_mode: int = 0) -> np.ndarray:
+    """u = code + zero-point = round(P * 2^d) (half up) for binary32 exponents d."""
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    u = np.empty(d.shape, np.uint8)
+    _check(lib().ora_pmap_p(_p(d), d.size, int(p_mode), _p(u)), "pmap")
     return u
 
 
@@ -207,7 +204,7 @@ def attention_rows(pro, b, h, rows, softmax_scale=None, with_m=False, p_mode=0, 
     _check(lib().ora_attention_head(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), N, D,
                                     scale, int(p_mode), int(bool(v_hadamard)), _p(rows), rows.size,
                                     _p(o), _p(m), -1,
-                                    None, None, None, None), "attention_head")
+                                    None, None, None, None, None), "attention_head")
     return (o, m) if with_m else o
 
 
@@ -215,7 +212,8 @@ def attention_tile(pro, b, h, q_blk, kv_blk, softmax_scale=None, p_mode=0):
     """Tile dump after key step kv_blk for the 64 query rows of q_blk.
 
     Rows past N are absent; returns dict of s_int [r,64], p_code [r,64],
-    pv_int [r,D], m_after [r] for the valid rows r."""
+    d_val [r,64] (the binary32 exponent of each key, -inf past N), pv_int [r,D],
+    m_after [r] for the valid rows r."""
     qc, sq, kc, sk, vc, sv = _head(pro, b, h)
     N, D = qc.shape
     scale = float(softmax_scale) if softmax_scale else 1.0 / np.sqrt(D)
@@ -225,13 +223,14 @@ def attention_tile(pro, b, h, q_blk, kv_blk, softmax_scale=None, p_mode=0):
     o = np.empty((n, D), np.float64)
     s_int = np.zeros((n, BLOCK), np.int32)
     p_code = np.zeros((n, BLOCK), np.int8)
+    d_val = np.zeros((n, BLOCK), np.float32)
     pv = np.zeros((n, D), np.int32)
     m_after = np.zeros(n, np.float32)
     _check(lib().ora_attention_head(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), N, D,
                                     scale, int(p_mode), 0, _p(rows), n, _p(o), None, int(kv_blk),
-                                    _p(s_int), _p(p_code), _p(pv), _p(m_after)),
+                                    _p(s_int), _p(p_code), _p(d_val), _p(pv), _p(m_after)),
            "attention_tile")
-    return dict(s_int=s_int, p_code=p_code, pv_int=pv, m_after=m_after)
+    return dict(s_int=s_int, p_code=p_code, d_val=d_val, pv_int=pv, m_after=m_after)
 
 
 def attention_full(pro, softmax_scale=None, p_mode=0, v_hadamard=False):
@@ -244,6 +243,22 @@ def attention_full(pro, softmax_scale=None, p_mode=0, v_hadamard=False):
             out[b, :, h, :] = attention_rows(pro, b, h, rows, softmax_scale, p_mode=p_mode,
                                              v_hadamard=v_hadamard)
     return out
+
+
+def code_digests(pro, b, h, rows, softmax_scale=None, p_mode=0):
+    """Per selected row of head (b, h): (sum of u over all keys, sum of
+    u * h(j) mod 2^32 with h(j) = 2654435761 (j + 1) mod 2^32, final running
+    max), u = code + zero-point -- a fingerprint of every P code of the row."""
+    qc, sq, kc, sk, _, _ = _head(pro, b, h)
+    N, D = qc.shape
+    scale = float(softmax_scale) if softmax_scale else 1.0 / np.sqrt(D)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    ds = np.empty(rows.size, np.uint32)
+    dh = np.empty(rows.size, np.uint32)
+    m = np.empty(rows.size, np.float32)
+    _check(lib().ora_code_digests(_p(qc), _p(sq), _p(kc), _p(sk), N, D, scale, int(p_mode),
+                                  _p(rows), rows.size, _p(ds), _p(dh), _p(m)), "code_digests")
+    return ds, dh, m
 
 
 def schedule_full_precision(sched, step, n_steps, block, n_blocks) -> bool:

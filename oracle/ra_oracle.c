@@ -37,10 +37,6 @@ enum { ORA_BLOCK = 64 };      /* tokens per Q/K scale block and per key step */
 enum { ORA_CODE_MAX = 7 };    /* symmetric INT4 codes in [-7, 7] */
 enum { ORA_MAX_D = 256 };
 
-/* Steps per log2 unit of the exponent grid on which P is evaluated. */
-enum { ORA_PGRID = 4755 };
-
-int ora_pgrid(void) { return ORA_PGRID; }
 int ora_block(void) { return ORA_BLOCK; }
 
 void ora_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }
@@ -293,74 +289,84 @@ static void fwht_f64(double *v, int D)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Range-optimized P map ([RA] Sec. 4.2: fixed scale 15, zero-point -8, so
- * p in [0,1] covers the whole signed INT4 range [-8, 7]).
- * code = round(15 p) - 8, p = 2^(x/G) with x the integer exponent on the grid
- * of G steps per log2 unit.  Rounding is half-up; u = code + 8 in [0, 15].
- * Written as a count of thresholds: u = #{k in 0..14 : x >= tau_k}, where
- * tau_k is the smallest integer with 15 * 2^(tau_k/G) >= k + 1/2.
+/* Range-optimized P map ([RA] Sec. 4.2 and the free-parameter ledger: fixed
+ * scale 15 and zero-point -8, so p in [0, 1] covers the whole signed INT4
+ * range [-8, 7]; abstract: p = exp(QK - max QK)).
+ *
+ * With the exponent d = log2 p (a binary32 value <= 0 in the attention
+ * below), code = round(15 * 2^d) - 8, rounding half up; u = code + 8 is in
+ * [0, 15].  The rounding is decided exactly by counting thresholds:
+ *   u = #{k in 0..14 : d >= T_k},
+ * where T_k is the smallest binary32 value with 15 * 2^T_k >= k + 1/2 in
+ * exact arithmetic (15 * 2^d >= k + 1/2 holds exactly for the d >= T_k).
  *
  * Symmetric P quantization (the baseline [RA] Sec. 4.2 replaces: P >= 0 on
- * a symmetric INT4 grid uses only the codes 0..7): code = u = round(7 p) in
- * [0, 7], zero-point 0; thresholds as above with 7 in place of 15.
- * ora_pmap_scale(mode) is the scale: 15 for mode 0, 7 for mode 1.          */
+ * a symmetric INT4 grid reaches only the codes 0..7): code = u = round(7 p)
+ * in [0, 7], zero-point 0; thresholds as above with 7 in place of 15.
+ * pmap_scale(mode) is the scale: 15 for mode 0, 7 for mode 1.
+ *
+ * The thresholds start from the binary64 logarithm and are moved one
+ * binary32 step at a time until P * 2^d >= k + 1/2 holds at T_k and fails
+ * one step below; the test uses exp2l (64-bit significand), far finer than
+ * the distance of any binary32 value from the exact boundary.               */
 static int pmap_scale(int p_mode) { return p_mode ? 7 : 15; }
 
-int ora_pmap_thresholds_p(int G, int p_mode, int32_t *tau)
+static int meets(float d, int P, int k)
 {
-    if (G < 1 || (p_mode != 0 && p_mode != 1)) return -1;
+    return (long double)P * exp2l((long double)d) >= (long double)k + 0.5L;
+}
+
+int ora_pmap_thresholds_p(int p_mode, float *T)
+{
+    if (p_mode != 0 && p_mode != 1) return -1;
     const int P = pmap_scale(p_mode);
     for (int k = 0; k < P; ++k) {
-        long double target = (long double)k + 0.5L;
-        long double t = log2l((long double)(2 * k + 1) / (2.0L * P)) * (long double)G;
-        long x = (long)ceill(t);
-        while ((long double)P * exp2l((long double)x / G) < target) ++x;
-        while ((long double)P * exp2l((long double)(x - 1) / G) >= target) --x;
-        tau[k] = (int32_t)x;
+        float d = (float)log2((double)(2 * k + 1) / (2.0 * P));
+        while (!meets(d, P, k)) d = nextafterf(d, INFINITY);
+        while (meets(nextafterf(d, -INFINITY), P, k)) d = nextafterf(d, -INFINITY);
+        T[k] = d;
     }
     return 0;
 }
 
-int ora_pmap_thresholds(int G, int32_t *tau) { return ora_pmap_thresholds_p(G, 0, tau); }
-
-static int pmap_u(float x, const int32_t *tau, int P)
+static int pmap_u(float d, const float *T, int P)
 {
     int u = 0;
     for (int k = 0; k < P; ++k)
-        if (x >= (float)tau[k]) ++u;
+        if (d >= T[k]) ++u;
     return u;
 }
 
-/* Vectorised form for tests: u[i] = map(x[i]) with the oracle's grid. */
-int ora_pmap_p(const float *x, int64_t n, int p_mode, uint8_t *u)
+/* Vectorised form for tests: u[i] = map(d[i]) (u = code + zero-point). */
+int ora_pmap_p(const float *d, int64_t n, int p_mode, uint8_t *u)
 {
-    int32_t tau[15];
-    if (ora_pmap_thresholds_p(ORA_PGRID, p_mode, tau)) return -1;
+    float T[15];
+    if (ora_pmap_thresholds_p(p_mode, T)) return -1;
     const int P = pmap_scale(p_mode);
-    for (int64_t i = 0; i < n; ++i) u[i] = (uint8_t)pmap_u(x[i], tau, P);
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) u[i] = (uint8_t)pmap_u(d[i], T, P);
     return 0;
 }
-
-int ora_pmap(const float *x, int64_t n, uint8_t *u) { return ora_pmap_p(x, n, 0, u); }
 
 /* ------------------------------------------------------------------------ */
 /* INT4 attention for one (b, h) slice, on selected query rows.
  *
  * Online softmax over key steps of 64 keys in ascending order (reading of
- * P = exp(QK - max(QK)) [RA abstract] inside a FlashAttention loop: the max
- * is the running max, updated once per 64-key step).
+ * p = exp(QK - max(QK)) [RA abstract] inside a FlashAttention loop: the max
+ * is the running max, updated once per 64-key step).  Exponents are in log2
+ * units, so p = 2^d.
  *   scores     S = sum_d qhat kc                               (exact int)
- *   c          = f32(f32(s_q s_k) * alphaG),
- *              alphaG = f32(log2(e) * softmax_scale * G)       (log2 units * G)
- *   step max   m_t = f32(max_j(S_j) * c), rounded to nearest;  m = max(m, m_t)
- *   exponent   x_j = RNE(f32(S_j c - m))  (single rounding of the exact value);
- *              a key whose S_j c lies above m (by at most half an ulp of m)
- *              has x_j >= 0 and, like the max itself, the top code
- *   P code     u_j = #{k : x_j >= tau_k}  in [0, 15]; code = u - 8
- *              (p_mode 1, symmetric: u_j in [0, 7], code = u, zero-point 0)
+ *   c          = f32(f32(s_q s_k) * alpha),
+ *              alpha = f32(log2(e) * softmax_scale)
+ *   step max   m_t = max over the step's keys of f32(S_j c);  m = max(m, m_t)
+ *              (m starts at -inf)
+ *   exponent   d_j = f32(S_j c - m): the exact value S_j c - m rounded once
+ *              to binary32 (d_j <= 0 up to half an ulp of m)
+ *   P code     u_j = round(15 * 2^d_j) by the thresholds above; code = u - 8
+ *              (p_mode 1, symmetric: u_j = round(7 * 2^d_j), code = u)
  *   sums       U = sum_j u_j;  num_c = sum_j u_j vhat_jc;
  *              PV_c = sum_j code_j vhat_jc = num_c - 8 sum_j vhat_jc
- *   float path (binary64):  beta = 2^((m_old - m)/G),
+ *   float path (binary64):  beta = 2^(m_old - m),
  *              A = A beta + num,  L = L beta + U,  o = A s_v / L,
  *              times H when the V codes are of V H (v_hadamard).
  * The dequantized P is u/15 (u/7), so the scale cancels in A/L: the row is
@@ -370,21 +376,22 @@ int ora_pmap(const float *x, int64_t n, uint8_t *u) { return ora_pmap_p(x, n, 0,
  * sv: [D].  rows: nrows query indices; o: [nrows, D] binary64.
  * m_out (optional): final running max per selected row (binary32).
  * Tile dump (optional, dbg_kb >= 0): for selected rows, after key step dbg_kb,
- * s_int[r*64 + j], p_code[r*64 + j] (-zero-point for keys >= N), pv_int[r*D + c],
+ * s_int[r*64 + j], p_code[r*64 + j] (-zero-point for keys >= N),
+ * d_val[r*64 + j] (the exponent d, -inf for keys >= N), pv_int[r*D + c],
  * m_after[r], indexed by r = position of the row in `rows`.                 */
 int ora_attention_head(const int8_t *qc, const float *sq,
                        const int8_t *kc, const float *sk,
                        const int8_t *vc, const float *sv,
                        int N, int D, double softmax_scale, int p_mode, int v_hadamard,
                        const int32_t *rows, int nrows, double *o, float *m_out,
-                       int dbg_kb, int32_t *s_int, int8_t *p_code,
+                       int dbg_kb, int32_t *s_int, int8_t *p_code, float *d_val,
                        int32_t *pv_int, float *m_after)
 {
     if (D > ORA_MAX_D || N < 1) return -1;
-    int32_t tau[15];
-    if (ora_pmap_thresholds_p(ORA_PGRID, p_mode, tau)) return -1;
+    float T[15];
+    if (ora_pmap_thresholds_p(p_mode, T)) return -1;
     const int P = pmap_scale(p_mode), zp = p_mode ? 0 : 8;
-    const float alphaG = (float)(M_LOG2E * softmax_scale * (double)ORA_PGRID);
+    const float alpha = (float)(M_LOG2E * softmax_scale);
     int nkb = (N + ORA_BLOCK - 1) / ORA_BLOCK;
 
     #pragma omp parallel for schedule(dynamic, 1)
@@ -395,6 +402,7 @@ int ora_attention_head(const int8_t *qc, const float *sq,
         float m = -INFINITY;
         double A[ORA_MAX_D], L = 0.0;
         int32_t S[ORA_BLOCK], u[ORA_BLOCK];
+        float dv[ORA_BLOCK];
         int64_t num[ORA_MAX_D];
         for (int c = 0; c < D; ++c) A[c] = 0.0;
 
@@ -402,30 +410,28 @@ int ora_attention_head(const int8_t *qc, const float *sq,
             int j0 = kb * ORA_BLOCK;
             int nj = (j0 + ORA_BLOCK < N ? ORA_BLOCK : N - j0);
             float sqk = sq[qb] * sk[kb];
-            float c = sqk * alphaG;
+            float c = sqk * alpha;
 
-            int32_t smax = INT32_MIN;
+            float mnew = m;
             for (int j = 0; j < nj; ++j) {
                 const int8_t *kj = kc + (size_t)(j0 + j) * D;
                 int64_t acc = 0;
                 for (int d = 0; d < D; ++d) acc += (int64_t)qi[d] * kj[d];
                 S[j] = (int32_t)acc;
-                if (S[j] > smax) smax = S[j];
+                float t = (float)((double)S[j] * (double)c);   /* exact product, one rounding */
+                if (t > mnew) mnew = t;
             }
-            float mt = (float)((double)smax * (double)c);   /* exact product, one rounding */
-            float mnew = m > mt ? m : mt;
 
             int64_t U = 0;
             for (int c2 = 0; c2 < D; ++c2) num[c2] = 0;
             for (int j = 0; j < nj; ++j) {
-                float dlt = fmaf((float)S[j], c, -mnew);
-                float x = rintf(dlt);
-                u[j] = pmap_u(x, tau, P);
+                dv[j] = fmaf((float)S[j], c, -mnew);           /* S c - m, one rounding */
+                u[j] = pmap_u(dv[j], T, P);
                 U += u[j];
                 const int8_t *vj = vc + (size_t)(j0 + j) * D;
                 for (int c2 = 0; c2 < D; ++c2) num[c2] += (int64_t)u[j] * vj[c2];
             }
-            double beta = exp2(((double)m - (double)mnew) / (double)ORA_PGRID);
+            double beta = exp2((double)m - (double)mnew);
             for (int c2 = 0; c2 < D; ++c2) A[c2] = A[c2] * beta + (double)num[c2];
             L = L * beta + (double)U;
             m = mnew;
@@ -435,6 +441,7 @@ int ora_attention_head(const int8_t *qc, const float *sq,
                     if (s_int) s_int[(size_t)r * ORA_BLOCK + j] = j < nj ? S[j] : 0;
                     if (p_code) p_code[(size_t)r * ORA_BLOCK + j] =
                         (int8_t)(j < nj ? u[j] - zp : -zp);
+                    if (d_val) d_val[(size_t)r * ORA_BLOCK + j] = j < nj ? dv[j] : -INFINITY;
                 }
                 if (pv_int)
                     for (int c2 = 0; c2 < D; ++c2) {
@@ -449,6 +456,58 @@ int ora_attention_head(const int8_t *qc, const float *sq,
         for (int c2 = 0; c2 < D; ++c2)
             o[(size_t)r * D + c2] = A[c2] * (double)sv[c2] / L;
         if (v_hadamard) fwht_f64(o + (size_t)r * D, D);   /* back from the rotated V basis */
+        if (m_out) m_out[r] = m;
+    }
+    return 0;
+}
+
+/* Integer digests of every P code of selected rows over all key steps:
+ * dig_sum[r] = sum_j u_j and dig_hash[r] = sum_j u_j * h(j) mod 2^32 with
+ * h(j) = (2654435761 * (j + 1)) mod 2^32, j the key index, u = code +
+ * zero-point.  A compact fingerprint of a whole row of codes for comparing
+ * long rows.  Same arithmetic as ora_attention_head; m_out as there.       */
+int ora_code_digests(const int8_t *qc, const float *sq, const int8_t *kc, const float *sk,
+                     int N, int D, double softmax_scale, int p_mode,
+                     const int32_t *rows, int nrows, uint32_t *dig_sum, uint32_t *dig_hash,
+                     float *m_out)
+{
+    if (D > ORA_MAX_D || N < 1) return -1;
+    float T[15];
+    if (ora_pmap_thresholds_p(p_mode, T)) return -1;
+    const int P = pmap_scale(p_mode);
+    const float alpha = (float)(M_LOG2E * softmax_scale);
+    int nkb = (N + ORA_BLOCK - 1) / ORA_BLOCK;
+
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r) {
+        int i = rows[r];
+        int qb = i / ORA_BLOCK;
+        const int8_t *qi = qc + (size_t)i * D;
+        float m = -INFINITY;
+        int32_t S[ORA_BLOCK];
+        uint32_t ds = 0, dh = 0;
+        for (int kb = 0; kb < nkb; ++kb) {
+            int j0 = kb * ORA_BLOCK;
+            int nj = (j0 + ORA_BLOCK < N ? ORA_BLOCK : N - j0);
+            float c = (sq[qb] * sk[kb]) * alpha;
+            float mnew = m;
+            for (int j = 0; j < nj; ++j) {
+                const int8_t *kj = kc + (size_t)(j0 + j) * D;
+                int64_t acc = 0;
+                for (int d = 0; d < D; ++d) acc += (int64_t)qi[d] * kj[d];
+                S[j] = (int32_t)acc;
+                float t = (float)((double)S[j] * (double)c);
+                if (t > mnew) mnew = t;
+            }
+            for (int j = 0; j < nj; ++j) {
+                uint32_t u = (uint32_t)pmap_u(fmaf((float)S[j], c, -mnew), T, P);
+                ds += u;
+                dh += u * (2654435761u * (uint32_t)(j0 + j + 1));
+            }
+            m = mnew;
+        }
+        dig_sum[r] = ds;
+        dig_hash[r] = dh;
         if (m_out) m_out[r] = m;
     }
     return 0;

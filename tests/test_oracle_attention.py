@@ -10,6 +10,7 @@ attention on well-conditioned data (error reported, loosely bounded).
 import numpy as np
 import pytest
 
+import brute_int4 as brute
 from oracle import ref_fp64 as ref
 
 
@@ -25,13 +26,18 @@ def _pro(qc, kc, vc, sq=None, sk=None, sv=None):
                 v_codes=vc[None, None].astype(np.int8), s_v=sv[None, None])
 
 
-def _alpha_g(ora, D):
-    return np.float32(np.log2(np.e) * (1.0 / np.sqrt(D)) * ora.pgrid())
+def _alpha(D):
+    return np.float32(np.log2(np.e) * (1.0 / np.sqrt(D)))
 
 
 def _rn32(exact):
     """The running max of a step: the scaled max score rounded to nearest."""
     return np.float32(exact)
+
+
+def _d(S, c, m):
+    """The exponent f32(S c - m): the exact value rounded once."""
+    return brute.f32_of_exact_sum(np.float64(S) * np.float64(c), -np.float64(m))
 
 
 def test_zero_queries_give_channel_means(ora):
@@ -76,10 +82,9 @@ def test_dominating_key_first(ora):
 @pytest.mark.parametrize("order", ["rising", "falling"])
 def test_two_tiles_of_equal_scores(ora, order):
     """Tile 0 keys all score a, tile 1 keys all score b.  With a rising max the
-    first tile is reweighted by beta = 2^((m0 - m1)/G); with a falling max the
+    first tile is reweighted by beta = 2^(m0 - m1); with a falling max the
     second tile's keys get the code of their exponent against m0.  The two
     query blocks carry different Q scales, so each row uses its own block's."""
-    G = ora.pgrid()
     D = 64
     N = 128
     a, b = (2, 7) if order == "rising" else (7, 2)
@@ -99,17 +104,17 @@ def test_two_tiles_of_equal_scores(ora, order):
     v0 = vc[:64].sum(axis=0).astype(np.float64)
     v1 = vc[64:].sum(axis=0).astype(np.float64)
     for qb in range(2):
-        c = np.float32(np.float32(sq[qb] * sk[0]) * _alpha_g(ora, D))
+        c = np.float32(np.float32(sq[qb] * sk[0]) * _alpha(D))
         m0 = _rn32(a * float(c))
         m1 = _rn32(b * float(c))
         rows = slice(qb * 64, qb * 64 + 64)
         if order == "rising":
-            beta = 2.0 ** ((float(m0) - float(m1)) / G)
+            beta = 2.0 ** (float(m0) - float(m1))
             want = (beta * 15 * v0 + 15 * v1) / (beta * 15 * 64 + 15 * 64)
             assert np.all(m[rows] == m1)
         else:
-            x = np.rint(np.float32(b * float(c) - float(m0)))
-            u1 = int(np.floor(15 * 2.0 ** (float(x) / G) + 0.5))
+            d = float(_d(b, c, m0))
+            u1 = int(np.floor(15 * 2.0 ** d + 0.5))
             assert 0 < u1 < 15
             want = (15 * v0 + u1 * v1) / (15 * 64 + u1 * 64)
             assert np.all(m[rows] == m0)
@@ -118,10 +123,9 @@ def test_two_tiles_of_equal_scores(ora, order):
 
 def test_keys_above_the_rounded_max_get_the_top_code(ora):
     """The step max is m = f32(S_max c), rounded to nearest.  With a large
-    score scale c it is coarse (an ulp of 8 grid units or more) and may lie
-    below S_max c; the max key then has x = rint(f32(S_max c - m)) >= 1 and
-    still gets the top code 15 - 8 = 7, while a key one score lower is
-    mapped against m as usual."""
+    score scale c it is coarse and may lie below S_max c; the max key then
+    has d = f32(S_max c - m) > 0 and still gets the top code 15 - 8 = 7,
+    while a key one score lower is mapped against m as usual."""
     D, N = 64, 64
     qc = np.zeros((N, D), int)
     qc[:, 0] = 7
@@ -133,16 +137,14 @@ def test_keys_above_the_rounded_max_get_the_top_code(ora):
     kc[9, 1] = -1                      # S = 48
     rng = np.random.default_rng(21)
     vc = rng.integers(-7, 8, size=(N, D))
-    alpha = np.float32(_alpha_g(ora, D))
-    G = ora.pgrid()
+    alpha = _alpha(D)
     picked = None
     for i in range(400):
-        s = np.float32(np.sqrt(2.0 ** 26 / (49 * float(alpha))) * (1.0 + i * 1e-4))
+        s = np.float32(np.sqrt(2.0 ** 14 / (49 * float(alpha))) * (1.0 + i * 1e-4))
         c = np.float32(np.float32(s * s) * alpha)
         exact = 49.0 * float(c)
         m = _rn32(exact)
-        x3 = np.rint(np.float32(exact - float(m)))
-        if float(m) < exact and x3 >= 1 and float(np.spacing(m)) >= 8.0:
+        if float(m) < exact:
             picked = (s, c, m)
             break
     assert picked is not None
@@ -150,9 +152,11 @@ def test_keys_above_the_rounded_max_get_the_top_code(ora):
     pro = _pro(qc, kc, vc, sq=[s], sk=[s])
     t = ora.attention_tile(pro, 0, 0, 0, 0)
     assert np.all(t["m_after"] == m)
+    assert np.all(t["d_val"][:, 3] > 0)
     assert np.all(t["p_code"][:, 3] == 7)
-    x9 = np.rint(np.float32(48.0 * float(c) - float(m)))
-    u9 = int(np.floor(15 * 2.0 ** (float(x9) / G) + 0.5)) if x9 < 0 else 15
+    d9 = float(_d(48, c, m))
+    assert np.all(t["d_val"][:, 9] == np.float32(d9))
+    u9 = int(np.floor(15 * 2.0 ** d9 + 0.5))
     assert np.all(t["p_code"][:, 9] == u9 - 8)
     assert np.all(t["p_code"][:, 0] == -8)
 
@@ -163,8 +167,9 @@ def test_tile_dump_integers(ora):
     qc = rng.integers(-7, 8, size=(N, D))
     kc = rng.integers(-7, 8, size=(N, D))
     vc = rng.integers(-7, 8, size=(N, D))
-    pro = _pro(qc, kc, vc, sq=rng.uniform(0.001, 0.01, 4), sk=rng.uniform(0.001, 0.01, 4))
+    pro = _pro(qc, kc, vc, sq=rng.uniform(0.05, 0.2, 4), sk=rng.uniform(0.05, 0.2, 4))
     prev = None
+    live = 0
     for kb in range(4):
         t = ora.attention_tile(pro, 0, 0, 1, kb)
         j0, j1 = kb * 64, min(N, kb * 64 + 64)
@@ -179,10 +184,18 @@ def test_tile_dump_integers(ora):
         if prev is not None:
             assert np.all(t["m_after"] >= prev)
         prev = t["m_after"]
+        # the exponent is S c - m rounded once, and the code its exact rounding
+        c = np.float32(np.float32(pro["s_q"][0, 0, 1] * pro["s_k"][0, 0, kb]) * _alpha(D))
+        d = _d(S, c, t["m_after"][:, None])
+        assert np.array_equal(t["d_val"][:, : j1 - j0].view(np.uint32), d.view(np.uint32))
+        u = np.floor(15 * np.exp2(d.astype(np.float64)) + 0.5)
+        assert np.array_equal(pc[:, : j1 - j0], u - 8)
+        live += int((u > 0).sum())
         # codes are monotone in the score within the tile
         for r in range(0, 64, 9):
             order = np.argsort(S[r], kind="stable")
             assert np.all(np.diff(pc[r, : j1 - j0][order]) >= 0)
+    assert live > 100
 
 
 def test_thread_count_does_not_change_results(ora):
