@@ -30,8 +30,10 @@ class Plan:
     """A validated problem (shape + options) with its RoPE tables.
 
     q, k, v, out are [B, N, H, D] contiguous CUDA tensors, N = F*H*W tokens in
-    (f, h, w) order.  rot: 'none' | 'interleaved' | 'half'; prec: 'int4' |
-    'bf16'; in_dtype/out_dtype: 'bf16' | 'f32'.
+    (f, h, w) order.  rot: 'none' | 'interleaved' | 'half' | 'full'; prec:
+    'int4' | 'bf16'; in_dtype/out_dtype: 'bf16' | 'f32'.  Creating a plan
+    copies its small RoPE tables to the current device; the calls then
+    allocate nothing on the library side.
     """
 
     def __init__(self, batch, heads, head_dim, grid, seg, rot="half", prec="int4",
@@ -83,15 +85,26 @@ class Plan:
                 raise ValueError("input must be a contiguous CUDA %s tensor of shape %s (got %s %s)"
                                  % (want, self.io_shape, t.dtype, tuple(t.shape)))
 
+    def _check_out(self, out, device):
+        want = _TORCH_DT[self.out_dtype]
+        if (tuple(out.shape) != self.io_shape or out.dtype != want or not out.is_contiguous()
+                or not out.is_cuda or out.device != device):
+            raise ValueError("out must be a contiguous %s tensor of shape %s on %s (got %s %s on %s)"
+                             % (want, self.io_shape, device, out.dtype, tuple(out.shape), out.device))
+
     def _ws(self, workspace, device):
         if workspace is None:
             workspace = self.workspace(device)
+        if (workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not workspace.is_cuda
+                or workspace.device != device):
+            raise ValueError("workspace must be a contiguous uint8 tensor on %s" % device)
         return workspace
 
     # -- calls --------------------------------------------------------------
     def forward(self, q, k, v, out=None, workspace=None, stream=None):
         self._check_in(q, k, v)
         out = self.empty_out(q.device) if out is None else out
+        self._check_out(out, q.device)
         ws = self._ws(workspace, q.device)
         check(lib().ra_attn_fwd(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
                                 ws.numel(), _stream_ptr(stream, q.device)), "ra_attn_fwd")
@@ -101,14 +114,22 @@ class Plan:
 
     def prologue(self, q, k, v, workspace, stream=None):
         self._check_in(q, k, v)
+        workspace = self._ws(workspace, q.device)
         check(lib().ra_attn_prologue(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(workspace),
                                      workspace.numel(), _stream_ptr(stream, q.device)),
               "ra_attn_prologue")
 
     def main(self, out, workspace, stream=None):
+        self._check_out(out, out.device)
+        workspace = self._ws(workspace, out.device)
         check(lib().ra_attn_main(self._h, _ptr(out), _ptr(workspace), workspace.numel(),
                                  _stream_ptr(stream, out.device)), "ra_attn_main")
         return out
+
+    def upload(self):
+        """Copy the plan's tables to the current device (needed before using
+        the plan on a device other than the one current at creation)."""
+        check(lib().ra_plan_upload(self._h), "ra_plan_upload")
 
     # -- parity exports -----------------------------------------------------
     def debug_prologue(self, q, k, v, workspace=None):
@@ -140,6 +161,19 @@ class Plan:
                                   _stream_ptr(None, workspace.device)), "ra_debug_tile")
         return dict(s_int=s_int, p_code=p_code, pv_int=pv, m_after=m)
 
+    def row_digests(self, workspace, out=None):
+        """Stage 2 through the parity variant of the INT4 kernel (f32
+        output): returns (out, rows) with rows [B, H, N, 4] uint32 = (final
+        running max bits, sum of u, sum of u * h(j) mod 2^32, row-sum bits)."""
+        B, N, H, D = self.io_shape
+        out = self.empty_out(workspace.device) if out is None else out
+        self._check_out(out, workspace.device)
+        workspace = self._ws(workspace, workspace.device)
+        rows = torch.empty((B, H, N, 4), dtype=torch.int32, device=workspace.device)
+        check(lib().ra_debug_row_digests(self._h, _ptr(out), _ptr(workspace), workspace.numel(), _ptr(rows),
+                                         _stream_ptr(None, workspace.device)), "ra_debug_row_digests")
+        return out, rows
+
     def tables(self, seg: int):
         npos = self.grid[seg]
         half = self.seg[seg] // 2
@@ -153,7 +187,21 @@ class Plan:
 def attn_fwd(q, k, v, grid, seg, rot="half", prec="int4", out_dtype="f32", workspace=None,
              stream=None):
     """One-shot forward through ra_attn_fwd_simple (plans cached in the library)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N, H, D] (got %s)" % (tuple(q.shape),))
     B, N, H, D = q.shape
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must be bfloat16 or float32 (got %s)" % q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("%s must be a %s tensor of shape %s on %s like q (got %s %s on %s)"
+                             % (name, q.dtype, tuple(q.shape), q.device, t.dtype, tuple(t.shape), t.device))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("%s must be a contiguous CUDA tensor" % name)
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()
+                                  or workspace.device != q.device):
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % q.device)
     in_dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}[q.dtype]
     shape = native.make_shape(B, H, D, grid, seg)
     opts = native.make_opts(rot, prec, in_dtype, out_dtype)
@@ -176,12 +224,17 @@ def schedule_pick(sched, step, n_steps, block, n_blocks) -> str:
     return "bf16" if lib().ra_schedule_pick(ctypes.byref(s), step, n_steps, block, n_blocks) else "int4"
 
 
-def pmap_device(x: torch.Tensor, p_mode: int = 0) -> torch.Tensor:
-    """The kernels' P map on grid exponents x (float32 CUDA tensor) -> u
-    (u = code + 8 for p_mode 0, u = code for p_mode 1)."""
-    x = x.contiguous()
-    u = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    check(lib().ra_debug_pmap(_ptr(x), _ptr(u), x.numel(), int(p_mode), _stream_ptr(None, x.device)),
+def pmap_device(d: torch.Tensor, p_mode: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The attention kernels' P map on exponents d = log2 p (float32 CUDA
+    tensor) -> u = round(15 2^d) = code + 8 (p_mode 0) or round(7 2^d) = code
+    (p_mode 1), uint8."""
+    if d.dtype != torch.float32 or not d.is_cuda:
+        raise ValueError("d must be a float32 CUDA tensor")
+    d = d.contiguous()
+    u = torch.empty(d.shape, dtype=torch.uint8, device=d.device) if out is None else out
+    if u.dtype != torch.uint8 or u.numel() != d.numel() or not u.is_contiguous() or u.device != d.device:
+        raise ValueError("out must be a contiguous uint8 tensor with d's size on its device")
+    check(lib().ra_debug_pmap(_ptr(d), _ptr(u), d.numel(), int(p_mode), _stream_ptr(None, d.device)),
           "ra_debug_pmap")
     return u
 
@@ -191,8 +244,11 @@ def copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int | None = None, stream
     check(lib().ra_copy(_ptr(dst), _ptr(src), nbytes, _stream_ptr(stream, src.device)), "ra_copy")
 
 
-def pgrid() -> int:
-    return int(lib().ra_pgrid())
+def pmap_thresholds(p_mode: int = 0) -> np.ndarray:
+    """The library's P-map thresholds T_k (binary32): u = #{k : d >= T_k}."""
+    T = np.empty(15 if p_mode == 0 else 7, np.float32)
+    check(lib().ra_pmap_thresholds(int(p_mode), T.ctypes.data_as(ctypes.c_void_p)), "ra_pmap_thresholds")
+    return T
 
 
 PEAK_KINDS = {"i8": 0, "fp8": 1, "fp6": 2, "fp6_fp8": 3, "bf16": 4}

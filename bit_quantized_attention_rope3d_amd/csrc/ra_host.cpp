@@ -50,6 +50,47 @@ bool inject(const char* what) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// ---- P map thresholds ([RA] Sec. 4.2: u = round(P p), p = 2^d, half up) --
+//
+// In terms of x = -d >= 0, u = #{k : x <= X_k} where X_k is the largest
+// binary32 x with P 2^-x >= k + 1/2.  Non-negative binary32 values are
+// ordered like their bit patterns, so X_k is found by bisection over bit
+// patterns between 0 (P 2^0 = P >= k + 1/2 for k < P) and 8 (P 2^-8 < 1/2),
+// the condition evaluated with a 64-bit-significand exp2l.
+float pmap_boundary(int P, int k) {
+  uint32_t lo = 0u, hi = 0x41000000u;   // bits of 0.0f and 8.0f
+  auto holds = [&](uint32_t b) {
+    float x;
+    std::memcpy(&x, &b, 4);
+    return (long double)P * exp2l(-(long double)x) >= (long double)k + 0.5L;
+  };
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + (hi - lo) / 2u;
+    if (holds(mid)) lo = mid;
+    else hi = mid;
+  }
+  float x;
+  std::memcpy(&x, &lo, 4);
+  return x;
+}
+
+// The attention kernels' table cell of x: rint(4096 x), ties to even (the
+// rounding the kernels' subnormal multiply performs; 4096 x is exact in
+// binary64).
+int pmap_cell(float x) { return (int)std::nearbyint((double)x * 4096.0); }
+
+ra::PMapArgs pmap_args(int p_mode) {
+  ra::PMapArgs pm{};
+  pm.P = p_mode ? 7 : 15;
+  for (int k = 0; k < pm.P; ++k) {
+    const float xk = pmap_boundary(pm.P, k);
+    pm.cell[k] = pmap_cell(xk);
+    pm.ythr[k] = xk * 0.125f;
+    if (pmap_cell(std::nextafter(xk, INFINITY)) == pm.cell[k]) pm.split |= 1u << k;
+  }
+  return pm;
+}
+
 struct Layout {
   int N, Npad, nblk, nkb, nqt;
   size_t off_q, off_k, off_v, off_sq, off_sk, off_sv, off_vamax, off_dbg, total;
@@ -136,7 +177,8 @@ struct ra_plan_s {
   int off[3];
   std::vector<float> cs[3], sn[3];
   size_t tab_floats;
-  float alpha_g, alpha;
+  float alpha;
+  ra::PMapArgs pm;
   std::mutex mu;
   std::map<int, float*> dev_tabs;
 };
@@ -172,31 +214,47 @@ void build_tables(ra_plan_s* p) {
   }
 }
 
-ra_status device_tables(ra_plan p, ra::RopeTabs* t) {
+// Copy the plan's RoPE tables to the current device, once per device
+// (allocates and synchronises: called from ra_plan_create and
+// ra_plan_upload, never from the forward entry points).
+ra_status upload_tables(ra_plan p) {
   if (inject("alloc")) return fail(RA_ERR_OOM, "injected allocation failure (RA_FAULT_INJECT=alloc)");
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(RA_ERR_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> g(p->mu);
-  auto it = p->dev_tabs.find(dev);
+  if (p->dev_tabs.count(dev)) return RA_OK;
   float* buf = nullptr;
-  if (it == p->dev_tabs.end()) {
-    if (hipMalloc(&buf, p->tab_floats * sizeof(float)) != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(RA_ERR_OOM, "hipMalloc of %zu bytes of RoPE tables failed", p->tab_floats * sizeof(float));
+  if (hipMalloc(&buf, p->tab_floats * sizeof(float)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(RA_ERR_OOM, "hipMalloc of %zu bytes of RoPE tables failed", p->tab_floats * sizeof(float));
+  }
+  std::vector<float> host;
+  host.reserve(p->tab_floats);
+  for (int s = 0; s < 3; ++s)      // (cos, sin) interleaved: one 8-byte load per pair
+    for (size_t i = 0; i < p->cs[s].size(); ++i) {
+      host.push_back(p->cs[s][i]);
+      host.push_back(p->sn[s][i]);
     }
-    std::vector<float> host;
-    host.reserve(p->tab_floats);
-    for (int s = 0; s < 3; ++s)      // (cos, sin) interleaved: one 8-byte load per pair
-      for (size_t i = 0; i < p->cs[s].size(); ++i) {
-        host.push_back(p->cs[s][i]);
-        host.push_back(p->sn[s][i]);
-      }
-    if (hipMemcpy(buf, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
-      hipFree(buf);
-      return fail(RA_ERR_HIP, "copying RoPE tables to device %d failed", dev);
-    }
-    p->dev_tabs[dev] = buf;
-  } else {
+  if (hipMemcpy(buf, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+    hipFree(buf);
+    return fail(RA_ERR_HIP, "copying RoPE tables to device %d failed", dev);
+  }
+  p->dev_tabs[dev] = buf;
+  return RA_OK;
+}
+
+// The current device's copy of the tables (no allocation, no copy).
+ra_status device_tables(ra_plan p, ra::RopeTabs* t) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(RA_ERR_HIP, "hipGetDevice failed");
+  float* buf = nullptr;
+  {
+    std::lock_guard<std::mutex> g(p->mu);
+    auto it = p->dev_tabs.find(dev);
+    if (it == p->dev_tabs.end())
+      return fail(RA_ERR_INVALID_ARG,
+                  "the plan has no tables on device %d: create it with that device current, "
+                  "or call ra_plan_upload there first", dev);
     buf = it->second;
   }
   const int dims[3] = {p->shape.grid_f, p->shape.grid_h, p->shape.grid_w};
@@ -242,10 +300,11 @@ ra::AttnArgs attn_args(ra_plan p, uint8_t* ws, void* o) {
   a.nblk = p->lay.nblk;
   a.nkb = p->lay.nkb;
   a.nqt = p->lay.nqt;
-  a.alpha_g = p->alpha_g;
   a.alpha = p->alpha;
   a.p_mode = p->opts.p_mode;
   a.v_hadamard = p->opts.v_hadamard;
+  a.pm = p->pm;
+  a.row_dbg = nullptr;
   return a;
 }
 
@@ -278,11 +337,32 @@ ra_status ra_plan_create(const ra_shape* shape, const ra_opts* opts, ra_plan* ou
   p->opts = *opts;
   p->lay = layout_of(shape, opts);
   const double scale = opts->softmax_scale > 0.0 ? opts->softmax_scale : 1.0 / std::sqrt((double)shape->head_dim);
-  p->alpha_g = (float)(M_LOG2E * scale * (double)ra::kPGrid);
   p->alpha = (float)(M_LOG2E * scale);
+  p->pm = pmap_args(opts->p_mode);
   build_tables(p);
+  // Tables go to the current device now, so that the forward calls neither
+  // allocate nor synchronise.  With no device present the plan still serves
+  // the host-side queries.
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) {
+    (void)hipGetLastError();
+    ndev = 0;
+  }
+  if (ndev > 0) {
+    st = upload_tables(p);
+    if (st != RA_OK) {
+      delete p;
+      return st;
+    }
+  }
   *out = p;
   return ok();
+}
+
+ra_status ra_plan_upload(ra_plan p) {
+  if (!p) return fail(RA_ERR_INVALID_ARG, "plan is null");
+  ra_status st = upload_tables(p);
+  return st == RA_OK ? ok() : st;
 }
 
 ra_status ra_plan_destroy(ra_plan p) {
@@ -449,7 +529,13 @@ const char* ra_status_str(ra_status s) {
 
 const char* ra_last_error_message(void) { return g_err.c_str(); }
 
-int32_t ra_pgrid(void) { return ra::kPGrid; }
+ra_status ra_pmap_thresholds(int32_t p_mode, float* T) {
+  if (p_mode != 0 && p_mode != 1) return fail(RA_ERR_INVALID_ARG, "p_mode %d is not 0 or 1", p_mode);
+  if (!T) return fail(RA_ERR_INVALID_ARG, "T is null");
+  const ra::PMapArgs pm = pmap_args(p_mode);
+  for (int k = 0; k < pm.P; ++k) T[k] = -pmap_boundary(pm.P, k);
+  return ok();
+}
 
 ra_status ra_debug_prologue(ra_plan p, const void* q, const void* k, const void* v, void* ws,
                             size_t ws_bytes, int8_t* q_codes, float* s_q, int8_t* k_codes,
@@ -554,11 +640,27 @@ ra_status ra_debug_tile(ra_plan p, void* ws, size_t ws_bytes, int32_t b, int32_t
   return ok();
 }
 
-ra_status ra_debug_pmap(const float* x, uint8_t* u, int64_t n, int32_t p_mode, hipStream_t stream) {
+ra_status ra_debug_row_digests(ra_plan p, void* o, void* ws, size_t ws_bytes, uint32_t* rows,
+                               hipStream_t stream) {
+  if (!p) return fail(RA_ERR_INVALID_ARG, "plan is null");
+  if (p->opts.prec != RA_PREC_INT4) return fail(RA_ERR_UNSUPPORTED, "row digests need an INT4 plan");
+  if (p->opts.out_dtype != RA_DT_F32) return fail(RA_ERR_UNSUPPORTED, "row digests need an f32-output plan");
+  if (!o || !rows) return fail(RA_ERR_INVALID_ARG, "o and rows must be non-null");
+  if (misaligned(o) || misaligned(rows)) return fail(RA_ERR_ALIGNMENT, "o and rows must be 16-byte aligned");
+  ra_status st = check_ws(p, ws, ws_bytes);
+  if (st != RA_OK) return st;
+  ra::AttnArgs a = attn_args(p, static_cast<uint8_t*>(ws), o);
+  a.row_dbg = rows;
+  ra::launch_int4_attn_rowdbg(a, p->shape.head_dim, p->shape.batch, stream);
+  st = after_launch("attention (row digests)");
+  return st == RA_OK ? ok() : st;
+}
+
+ra_status ra_debug_pmap(const float* d, uint8_t* u, int64_t n, int32_t p_mode, hipStream_t stream) {
   if (n < 0) return fail(RA_ERR_INVALID_ARG, "n must be >= 0");
-  if (n > 0 && (!x || !u)) return fail(RA_ERR_INVALID_ARG, "x and u must be non-null");
+  if (n > 0 && (!d || !u)) return fail(RA_ERR_INVALID_ARG, "d and u must be non-null");
   if (p_mode != 0 && p_mode != 1) return fail(RA_ERR_INVALID_ARG, "p_mode %d is not 0 or 1", p_mode);
-  ra::launch_pmap_probe(x, u, n, p_mode, stream);
+  ra::launch_pmap_probe(d, u, n, pmap_args(p_mode), stream);
   ra_status st = after_launch("pmap probe");
   return st == RA_OK ? ok() : st;
 }

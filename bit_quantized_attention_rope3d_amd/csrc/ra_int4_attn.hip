@@ -23,12 +23,14 @@
 //     an integer below 2^24, so the fp32 accumulator holds the exact integer
 //     score and no int->float conversion is needed.  Each lane holds one
 //     query column, so the row max is in-lane (+1 cross-half swap).
-//   * P codes come straight out of the accumulator registers: the distance
-//     of each score below the running max, rounded to the exponent grid, is
-//     turned into a table index by one clamped FMA and one multiply into the
-//     fp32 subnormal range (whose bit pattern is then the rounded index), and
-//     looked up in a 32 KB byte table of u as e4m3 at LDS address 0, built
-//     per workgroup from the exp2 form of the map.  Two byte permutes and an
+//   * P codes come straight out of the accumulator registers: the exponent
+//     d = f32(S c - m) of each score (one FMA) is turned into a table index
+//     j = rint(-4096 d) by a multiply into the fp32 subnormal range (whose
+//     bit pattern is then the rounded index), and looked up in a 32 KB byte
+//     table of u = round(15 2^d) as e4m3 at LDS address 0.  Fifteen table
+//     cells hold a rounding boundary of 15 2^d inside them; their entries
+//     are marked, and the few scores that land in one are decided exactly by
+//     an fp32 compare of d against the boundary.  Two byte permutes and an
 //     OR pack four codes in the order the PV MFMA wants them as its B
 //     operand; V is stored pre-permuted to match.
 //   * PV = V^T P^T runs on the same MFMA with V in fp6 and P in fp8 (u in
@@ -67,34 +69,44 @@ struct State {
 
 // ---- range-optimized P map through an LDS table --------------------------
 //
-// For a score S with scale c and running max m (grid units), the grid
-// exponent is x = rint(f32(S c - m)) <= 0 and the code is u(x); u(x) = 0 for
-// every x <= -2^15, so a table of u(-j), j = 0..2^15, covers all scores.
-// With c' = c 2^-15 and m' = m 2^-15 (exact power-of-two scalings):
-//   y = clamp(fma(S, -c', m'))   f32(m - S c) 2^-15 clamped to [0, 1]:
-//                                keys at or above the running max (the
-//                                scaled max rounded to nearest, so a key
-//                                may exceed it by half an ulp) give 0, the
-//                                top code, far keys saturate at 1, and with
+// For a score S with scale c and running max m (log2 units), the exponent
+// is d = f32(S c - m) and u = round(P 2^d) = #{k : x <= X_k} with x = -d
+// (PMapArgs).  With c' = c / 8 and m' = m / 8 (exact power-of-two scalings):
+//   y = clamp(fma(S, -c', m'))   f32(m - S c) / 8 = x / 8, clamped to
+//                                [0, 1]: keys at or above the running max
+//                                (d >= 0) give 0, the top code; x >= 8 (no
+//                                code above 0 there) saturates at 1; with
 //                                the DX10 clamp mode of compute kernels a
-//                                NaN or a -0 becomes +0, so y is in [+0, 1]
-//                                for every input
+//                                NaN or a -0 becomes +0
 //   w = y 2^-134                 subnormal (f32 denormals are enabled in
 //                                these kernels), spacing 2^-149 = 2^-15 of
-//                                y: the product rounds f32(m - S c) to the
-//                                nearest integer, ties to even, as rint,
-//                                and bits(w) = -x = j in [0, 2^15]
+//                                y: the product rounds 4096 x to the
+//                                nearest integer, ties to even, and
+//                                bits(w) = j in [0, 2^15]
 // The table sits at LDS address 0, so j is the byte address of its entry.
-// The running max is passed as m' + 0, which turns a -0 into +0.
+// Scalings by 1/8 are exact unless a value is below 2^-123, and then x is
+// far below the smallest X_k and every path gives cell 0 and u = P.  The
+// running max is passed as m' + 0, which turns a -0 into +0.
+//
+// Entry j is e4m3(u) when every x of cell j has the same u; in the cell of
+// an X_k that also holds values above it, the entry is 0x80 | k (no e4m3
+// code of 0..15 has bit 7 set) and u = k + (y <= X_k / 8), decided by
+// pmap_fix after the lookup from the 8-byte record k behind the table:
+// X_k / 8, then the bytes e4m3(k) and e4m3(k + 1).
 constexpr int kPTabSpan = 1 << 15;
 constexpr int kPTabEntries = kPTabSpan + 1;                 // j = 0..2^15
 constexpr int kPTabBytes = (kPTabEntries + 15) & ~15;       // one byte each, 16-byte padded
-constexpr float kPTabScale = 1.0f / 32768.0f;               // 2^-15
+constexpr int kPThrBytes = 16 * 8;                          // 16 records behind the table
+constexpr float kPIdxScale = 0.125f;                        // 2^-3
+constexpr uint32_t kPSplit = 0x80808080u;                   // marked entries, per packed byte
+
+__device__ __forceinline__ float pmap_y(float s, float c2, float m2) {
+  // med3(x, 0, 1) folds into the clamp bit of the FMA (DX10 clamp mode).
+  return __builtin_amdgcn_fmed3f(__builtin_fmaf(s, -c2, m2), 0.0f, 1.0f);
+}
 
 __device__ __forceinline__ uint32_t ptab_addr(float s, float c2, float m2) {
-  // med3(x, 0, 1) folds into the clamp bit of the FMA (DX10 clamp mode).
-  const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(s, -c2, m2), 0.0f, 1.0f);
-  return __float_as_uint(y * 0x1p-134f);
+  return __float_as_uint(pmap_y(s, c2, m2) * 0x1p-134f);
 }
 
 // e4m3 encoding of an integer 0 <= u <= 15 (exact).
@@ -111,20 +123,34 @@ __device__ __forceinline__ uint32_t e4m3_to_uint(uint32_t b) {
   return ((8u | m) << e) >> 3;
 }
 
-// Fill the table cooperatively (threads tid, tid + nt, ...) from the exp2
-// form of the map, exact on every grid point: entry j = e4m3(u) | u << 8 for
-// u = u(-j).
-__device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt, int p_mode) {
-  const float log2p = p_mode ? kLog2Of7 : kLog2Of15;
+// Fill the table and the thresholds behind it cooperatively (threads tid,
+// tid + nt, ...): entry j counts the X_k whose cell lies above j (cell j
+// holds only x below them), plus the X_k whose cell is j when that cell
+// holds nothing above it; a cell that does is marked with its k.
+__device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt, const PMapArgs& pm) {
   for (int j = tid; j < kPTabEntries; j += nt) {
-    const uint32_t u = pmap_insert(-(float)j, 0u, 0u, log2p) & 0xFFu;
-    tab[j] = (uint8_t)e4m3_of_uint(u);
+    uint32_t u = 0, mark = 0;
+    for (int k = 0; k < pm.P; ++k) {
+      const bool split = (pm.split >> k) & 1u;
+      if (j < pm.cell[k] || (j == pm.cell[k] && !split)) ++u;
+      if (j == pm.cell[k] && split) mark = 0x80u | (uint32_t)k;
+    }
+    tab[j] = (uint8_t)(mark ? mark : e4m3_of_uint(u));
+  }
+  uint32_t* rec = reinterpret_cast<uint32_t*>(tab + kPTabBytes);
+  for (int k = tid; k < 16; k += nt) {
+    rec[2 * k] = __float_as_uint(k < pm.P ? pm.ythr[k] : 0.0f);
+    rec[2 * k + 1] = e4m3_of_uint((uint32_t)k) | (e4m3_of_uint((uint32_t)k + 1u) << 8);
   }
 }
 
 // ---- K/V staging: global memory -> LDS without registers ------------------
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+// LDS address (offset in the workgroup's LDS) of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
 // 16-byte buffer load with the LDS-direct bit: lane i copies 16 bytes from
 // base(rsrc) + voffset into LDS at lds + 16 i (lds is wave-uniform).  It is
 // written as an instruction the compiler does not model as a store to LDS:
@@ -133,8 +159,8 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // is every read of the other stages.  Completion is ordered explicitly by
 // wait_lds_dma() and the workgroup barrier; no register receives data, and
 // M0 is set and used inside the statement.
-__device__ __forceinline__ void lds_copy16(v4i rsrc, const uint8_t* lds, int voffset) {
-  const uint32_t m = (uint32_t)(uintptr_t)(const lds_u8*)lds;
+__device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t lds, int voffset) {
+  const uint32_t m = lds;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(m), "v"(voffset), "s"(rsrc)
@@ -192,8 +218,8 @@ struct TileDma {
   }
 
   // K tile at kt -> kst, V tile at vt -> vst (global addresses of the
-  // tiles); a null tile is skipped.
-  __device__ __forceinline__ void issue(const uint8_t* kt, const uint8_t* vt, uint8_t* kst, uint8_t* vst) const {
+  // tiles, LDS addresses of the stages); a null tile is skipped.
+  __device__ __forceinline__ void issue(const uint8_t* kt, const uint8_t* vt, uint32_t kst, uint32_t vst) const {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       if (kind[j] == 1 && kt != nullptr)
@@ -232,10 +258,9 @@ __device__ __forceinline__ int acc_key(int mt, int r, int hf) {
 // loop-invariant register per read and re-adds the stage offset to each,
 // instead of one add per base and the constants in the read instructions.
 typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
-__device__ __forceinline__ lds_cu8* lds_base(const uint8_t* p) {
-  uint32_t a = (uint32_t)(uintptr_t)(lds_cu8*)p;
+__device__ __forceinline__ lds_cu8* lds_base(uint32_t a) {
   asm("" : "+v"(a));
-  return (lds_cu8*)(uintptr_t)a;
+  return (lds_cu8*)a;
 }
 template <typename T>
 __device__ __forceinline__ T lds_ld(lds_cu8* p) {
@@ -247,6 +272,24 @@ __device__ __forceinline__ T lds_ld(lds_cu8* p) {
 // registers of an fp6 operand must be consecutive).  No instruction.
 __device__ __forceinline__ void operand_fence() { asm volatile("" ::: "memory"); }
 
+// This lane's byte offsets inside a K stage (fp6 K operand: 16-byte and
+// 8-byte part) and a V stage (fp6 V operand), computed once and hidden from
+// the optimizer, so that each step adds the stage address to each of them
+// once and the compiler keeps no further copies of them.
+struct LaneLds {
+  uint32_t klo, khi, vlo, vhi;
+};
+__device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+template <int D>
+__device__ __forceinline__ LaneLds lane_lds() {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
+  return LaneLds{opaque_v((uint32_t)qk6_lo_off(ln, hf)), opaque_v((uint32_t)qk6_hi_off(D, ln, hf)),
+                 opaque_v((uint32_t)v6_lo_off(D, ln, hf)), opaque_v((uint32_t)v6_hi_off(D, ln, hf))};
+}
+
 // ---- building blocks of one 64-key step for the 32 queries of a wave ------
 
 // S^T of the step (exact integers in fp32): kst is the step's fp6 K tile.
@@ -255,10 +298,9 @@ __device__ __forceinline__ void operand_fence() { asm volatile("" ::: "memory");
 // addresses (no bank conflicts without a swizzle).  Both offsets are linear
 // in (row, group), so one lane base per part plus constants covers all reads.
 template <int D>
-__device__ __forceinline__ void qk_step(const uint8_t* kst, const v8i (&qop)[Cfg<D>::QC], v16f (&s)[2]) {
-  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
-  lds_cu8* const klo = lds_base(kst + qk6_lo_off(ln, hf));
-  lds_cu8* const khi = lds_base(kst + qk6_hi_off(D, ln, hf));
+__device__ __forceinline__ void qk_step(uint32_t kst, const LaneLds& ll, const v8i (&qop)[Cfg<D>::QC], v16f (&s)[2]) {
+  lds_cu8* const klo = lds_base(kst + ll.klo);
+  lds_cu8* const khi = lds_base(kst + ll.khi);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -294,13 +336,14 @@ __device__ __forceinline__ void mask_scores(v16f (&s)[2], int nvalid) {
       if (acc_key(mt, r, hf) >= nvalid) s[mt][r] = -INFINITY;
 }
 
-// New running max for this lane's query (grid units): the larger of m and
-// f32(max_j S_j * c), rounded to nearest.
+// New running max for this lane's query (log2 units): the larger of m and
+// f32(max_j S_j * c) (rounded to nearest; + 0 makes a -0 product +0, so
+// that the max never has to order zeros of both signs).
 __device__ __forceinline__ float running_max(const v16f (&s)[2], float c, float m) {
   float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
   for (int k = 2; k < 32; ++k) mx = fmaxf(mx, s[k >> 4][k & 15]);
-  return fmaxf(m, xhalf_max_f(mx) * c);
+  return fmaxf(m, xhalf_max_f(mx) * c + 0.0f);
 }
 
 // P codes of a whole step (u in e4m3, both M-tiles) in the order of the PV
@@ -308,6 +351,7 @@ __device__ __forceinline__ float running_max(const v16f (&s)[2], float c, float 
 // All 32 table loads are issued before any is used, so the LDS latency is
 // paid once per step; each load leaves one byte in the low end of its
 // register, and two v_perm (bytes 0-1 and 2-3) and an OR pack four of them.
+// Marked entries (bit 7) still need pmap_fix.
 __device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c2, float m2, const uint8_t* tab,
                                           uint32_t (&p)[2][4]) {
   uint32_t x[32];
@@ -317,6 +361,45 @@ __device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c2, float m2
   for (int w = 0; w < 8; ++w)
     p[w >> 2][w & 3] = __builtin_amdgcn_perm(x[4 * w + 1], x[4 * w], 0x0C0C0400u) |
                        __builtin_amdgcn_perm(x[4 * w + 3], x[4 * w + 2], 0x04000C0Cu);
+}
+
+// Whether any lane of the wave holds a marked entry (wave-uniform).
+__device__ __forceinline__ bool pmap_marked(const uint32_t (&p)[2][4]) {
+  const uint32_t o = (p[0][0] | p[0][1] | p[0][2] | p[0][3]) | (p[1][0] | p[1][1] | p[1][2] | p[1][3]);
+  return __builtin_amdgcn_ballot_w64((o & kPSplit) != 0u) != 0u;
+}
+
+// Decide the marked entries exactly: the entry 0x80 | k stands for
+// u = k + (x <= X_k), i.e. k + (y <= X_k / 8) with y as in the lookup.  A
+// packed word is revisited only when some lane has a marked byte in it; its
+// four bytes are then decided without branches (unmarked bytes keep theirs).
+__device__ __forceinline__ void pmap_fix(const v16f (&s)[2], float c2, float m2, const uint8_t* recs,
+                                         uint32_t (&p)[2][4]) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t pw = p[w >> 2][w & 3];
+    if (__builtin_amdgcn_ballot_w64((pw & kPSplit) != 0u) != 0u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b = (pw >> (8 * e)) & 0xFFu;
+        if (b & 0x80u) {
+          const float thr = *reinterpret_cast<const float*>(recs + 8 * (b & 0x0Fu));
+          const float y = pmap_y(s[w >> 2][4 * (w & 3) + e], c2, m2);
+          const uint32_t nb = e4m3_of_uint((b & 0x0Fu) + (y <= thr ? 1u : 0u));
+          pw = __builtin_amdgcn_perm(nb, pw, (0x03020100u & ~(0xFFu << (8 * e))) | (0x04u << (8 * e)));
+        }
+      }
+      p[w >> 2][w & 3] = pw;
+    }
+  }
+}
+
+// The whole P map of a step: lookups, then the exact decision of marked
+// entries when the wave has any (rare: 15 cells of 2^15).
+__device__ __forceinline__ void pmap_codes(const v16f (&s)[2], float c2, float m2, const uint8_t* tab,
+                                           uint32_t (&p)[2][4]) {
+  pmap_step(s, c2, m2, tab, p);
+  if (__builtin_expect(pmap_marked(p), 0)) pmap_fix(s, c2, m2, tab + kPTabBytes, p);
 }
 
 // Zero the P codes of keys at or past nvalid (ragged last step).
@@ -357,13 +440,12 @@ __device__ __forceinline__ void lsum_step(const v8i& sel, const uint32_t (&p)[2]
 // supplies the fp6 string of channel 32 dt + ln, half hf: one 16-byte and
 // one 8-byte read, tile dt 512 and 256 bytes past the lane bases.
 template <int D>
-__device__ __forceinline__ void pv_step(const uint8_t* vst, const uint32_t (&p)[2][4],
+__device__ __forceinline__ void pv_step(uint32_t vst, const LaneLds& ll, const uint32_t (&p)[2][4],
                                         v16f (&acc)[Cfg<D>::DT]) {
-  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const v8i pb = v8i{(int)p[0][0], (int)p[0][1], (int)p[0][2], (int)p[0][3],
                      (int)p[1][0], (int)p[1][1], (int)p[1][2], (int)p[1][3]};
-  lds_cu8* const vlo = lds_base(vst + v6_lo_off(D, ln, hf));
-  lds_cu8* const vhi = lds_base(vst + v6_hi_off(D, ln, hf));
+  lds_cu8* const vlo = lds_base(vst + ll.vlo);
+  lds_cu8* const vhi = lds_base(vst + ll.vhi);
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
     const v4i lo = lds_ld<v4i>(vlo + 512 * dt);
@@ -378,7 +460,7 @@ __device__ __forceinline__ void pv_step(const uint8_t* vst, const uint32_t (&p)[
 // beta = 0 on the first step (st.m = -inf).
 template <int D>
 __device__ __forceinline__ void rescale(State<D>& st, float m_new) {
-  const float beta = exp2f((st.m - m_new) * kInvPGrid);
+  const float beta = exp2f(st.m - m_new);
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt)
 #pragma unroll
@@ -386,33 +468,34 @@ __device__ __forceinline__ void rescale(State<D>& st, float m_new) {
   st.lsum *= beta;
 }
 
-// c = f32(f32(s_q s_k) alpha_G): grid units per unit of integer score.
-__device__ __forceinline__ float score_scale(float cq, float sk, float alpha_g) {
+// c = f32(f32(s_q s_k) alpha): log2 units per unit of integer score.
+__device__ __forceinline__ float score_scale(float cq, float sk, float alpha) {
   const float sqk = cq * sk;
-  return sqk * alpha_g;
+  return sqk * alpha;
 }
 
 // One whole 64-key step in program order (used by the parity dump kernel;
 // the main kernel runs the same blocks software-pipelined).
 template <int D, bool DUMP>
-__device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst, const uint8_t* tab,
-                                          const v8i (&qop)[Cfg<D>::QC], float cq, float alpha_g,
+__device__ __forceinline__ void tile_step(uint32_t kst, uint32_t vst, const uint8_t* tab,
+                                          const v8i (&qop)[Cfg<D>::QC], float cq, float alpha,
                                           float sk, int nvalid, State<D>& st,
-                                          const TileDumpArgs* dump, int wave, int p_mode) {
-  const int zp = p_mode ? 0 : 8;                   // code = u - zp
+                                          const TileDumpArgs* dump, int wave, int P) {
+  const int zp = P == 15 ? 8 : 0;                  // code = u - zp
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   v16f s[2];
-  qk_step<D>(kst, qop, s);
+  const LaneLds ll = lane_lds<D>();
+  qk_step<D>(kst, ll, qop, s);
   if (nvalid < kBlock) mask_scores(s, nvalid);
-  const float cp = score_scale(cq, sk, alpha_g);
+  const float cp = score_scale(cq, sk, alpha);
   const float m_new = running_max(s, cp, st.m);
   if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
   st.m = m_new;
   uint32_t p[2][4];
-  pmap_step(s, cp * kPTabScale, m_new * kPTabScale + 0.0f, tab, p);
+  pmap_codes(s, cp * kPIdxScale, m_new * kPIdxScale + 0.0f, tab, p);
   if (nvalid < kBlock) mask_p(p, nvalid);
-  pv_step<D>(vst, p, st.acc);
+  pv_step<D>(vst, ll, p, st.acc);
   lsum_step(lsum_selector(), p, st.lsum);
 
   if (DUMP) {
@@ -437,8 +520,8 @@ __device__ __forceinline__ void tile_step(const uint8_t* kst, const uint8_t* vst
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) { pv[dt][r] = 0.0f; cs[dt][r] = 0.0f; }
-    pv_step<D>(vst, p, pv);
-    pv_step<D>(vst, ones, cs);
+    pv_step<D>(vst, ll, p, pv);
+    pv_step<D>(vst, ll, ones, cs);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -509,14 +592,36 @@ __device__ __forceinline__ void state_init(State<D>& st) {
   st.lsum = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-template <int D, bool OUT_BF16, bool VH>
+// Parity variant only: fingerprints of every P code of this lane's query
+// (u = code + zero-point): the sum of u and the sum of u h(j) mod 2^32 with
+// h(j) = 2654435761 (j + 1), j the key index.  Keys past N carry u = 0.
+__device__ __forceinline__ void row_digest(const uint32_t (&p)[2][4], int t, uint32_t& ds, uint32_t& dh) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t u = e4m3_to_uint((p[mt][r >> 2] >> (8 * (r & 3))) & 0xFFu);
+      const uint32_t key = (uint32_t)(t * kBlock + acc_key(mt, r, hf));
+      ds += u;
+      dh += u * (2654435761u * (key + 1u));
+    }
+}
+
+__device__ __forceinline__ uint32_t xhalf_sum_u(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((int)x, (int)x, false, false);
+  return (uint32_t)r[0] + (uint32_t)r[1];
+}
+
+// DUMP: the parity variant -- the same kernel (same ring, barriers, peeled
+// steps and workgroup order) that also writes, per query row, its final
+// running max, the two P-code fingerprints and its row sum to a.row_dbg.
+template <int D, bool OUT_BF16, bool VH, bool DUMP>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kPTabBytes + kStages * (C::KT + C::VT)];
-  uint8_t* const ptab = smem;                               // P-map table at LDS address 0
-  uint8_t* const kbuf = smem + kPTabBytes;                  // K stages
-  uint8_t* const vbuf = smem + kPTabBytes + kStages * C::KT;   // V stages
-  ptab_build(ptab, threadIdx.x, 64 * kWaves, a.p_mode);     // visible after the first barrier
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPTabBytes + kPThrBytes + kStages * (C::KT + C::VT)];
+  uint8_t* const ptab = smem;                               // P-map table at LDS address 0, then K and V stages
+  ptab_build(ptab, threadIdx.x, 64 * kWaves, a.pm);         // visible after the first barrier
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of (head, query-tile) ids.
@@ -545,6 +650,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   State<D> st;
   state_init<D>(st);
   const v8i lsel = lsum_selector();
+  uint32_t dsum = 0, dhash = 0;                             // DUMP only
 
   // Step t: P codes of step t (S in registers), S of step t+1, P x V of step
   // t, then the running max of step t+1 and the rescale it may need.  Within
@@ -560,8 +666,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   const TileDma<D, kWaves> dma;
   const uint8_t* const ktiles = a.kp + (size_t)bh * a.nblk * C::KT;
   const uint8_t* const vtiles = a.vp + (size_t)bh * a.nkb * C::VT;
-  auto kst = [&](int t) { return kbuf + (t % kStages) * C::KT; };
-  auto vst = [&](int t) { return vbuf + (t % kStages) * C::VT; };
+  // smem is the kernel's only LDS variable, at LDS address 0 (the P-map
+  // lookup relies on it), so the stages' LDS addresses are constants.
+  constexpr uint32_t kbase = kPTabBytes + kPThrBytes, vbase = kbase + kStages * C::KT;
+  auto kst = [&](int t) { return kbase + (uint32_t)((t % kStages) * C::KT); };
+  auto vst = [&](int t) { return vbase + (uint32_t)((t % kStages) * C::VT); };
   dma.issue(ktiles, nullptr, kst(0), vst(0));
   wait_lds_dma();
   __syncthreads();
@@ -570,12 +679,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     dma.issue(i < nkb ? ktiles + i * C::KT : nullptr, i - 1 < nkb ? vtiles + (i - 1) * C::VT : nullptr,
               kst(i), vst(i - 1));
   v16f s[2];
-  qk_step<D>(kst(0), qop, s);
+  const LaneLds ll = lane_lds<D>();
+  qk_step<D>(kst(0), ll, qop, s);
   {
     const int nv0 = min(kBlock, a.N);
     if (nv0 < kBlock) mask_scores(s, nv0);
   }
-  float cp_cur = score_scale(cq, sk[0], a.alpha_g);
+  float cp_cur = score_scale(cq, sk[0], a.alpha);
   st.m = running_max(s, cp_cur, -INFINITY);
   wait_lds_dma();
   __syncthreads();
@@ -586,15 +696,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     dma.issue(t + kSync + 1 < nkb ? ktn : nullptr, t + kSync < nkb ? vtn : nullptr, kst(t + kSync + 1),
               vst(t + kSync));
     uint32_t p[2][4];
-    pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale + 0.0f, ptab, p);
-    qk_step<D>(kst(t + 1), qop, s);       // S of step t+1
-    pv_step<D>(vst(t), p, st.acc);
+    pmap_codes(s, cp_cur * kPIdxScale, st.m * kPIdxScale + 0.0f, ptab, p);
+    if constexpr (DUMP) row_digest(p, t, dsum, dhash);
+    qk_step<D>(kst(t + 1), ll, qop, s);   // S of step t+1
+    pv_step<D>(vst(t), ll, p, st.acc);
     lsum_step(lsel, p, st.lsum);
     if constexpr (decltype(ragged)::value) {
       const int nv1 = a.N - (t + 1) * kBlock;
       if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
     }
-    const float cp_next = score_scale(cq, sk[t + 1], a.alpha_g);
+    const float cp_next = score_scale(cq, sk[t + 1], a.alpha);
     const float m_new = running_max(s, cp_next, st.m);
     if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
     st.m = m_new;
@@ -621,10 +732,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     // The last step: its V tile is resident since the barrier before it.
     const int t = nkb - 1, nvalid = a.N - t * kBlock;
     uint32_t p[2][4];
-    pmap_step(s, cp_cur * kPTabScale, st.m * kPTabScale + 0.0f, ptab, p);
+    pmap_codes(s, cp_cur * kPIdxScale, st.m * kPIdxScale + 0.0f, ptab, p);
     if (nvalid < kBlock) mask_p(p, nvalid);
-    pv_step<D>(vst(t), p, st.acc);
+    if constexpr (DUMP) row_digest(p, t, dsum, dhash);
+    pv_step<D>(vst(t), ll, p, st.acc);
     lsum_step(lsel, p, st.lsum);
+  }
+
+  if constexpr (DUMP) {
+    dsum = xhalf_sum_u(dsum);
+    dhash = xhalf_sum_u(dhash);
+    const int q = q0 + ln;
+    if (hf == 0 && q < a.N) {
+      uint32_t* r = a.row_dbg + ((size_t)bh * a.N + q) * 4;
+      *reinterpret_cast<uint4*>(r) = make_uint4(__float_as_uint(st.m), dsum, dhash, __float_as_uint(st.lsum[0]));
+    }
   }
 
   // o = A s_v / L: the scale of the dequantized P cancels against the
@@ -678,10 +800,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs t) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kPTabBytes + C::KT + C::VT];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPTabBytes + kPThrBytes + C::KT + C::VT];
   uint8_t* const ptab = smem;
-  uint8_t* const tiles = smem + kPTabBytes;
-  ptab_build(ptab, threadIdx.x, 128, a.p_mode);
+  constexpr uint32_t kTiles = kPTabBytes + kPThrBytes;     // LDS address of the K tile, then V
+  ptab_build(ptab, threadIdx.x, 128, a.pm);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const int bh = t.bh;
   const int q0 = t.q_blk * kBlock + wave * 32;
@@ -692,30 +814,42 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   state_init<D>(st);
   const TileDma<D, 2> dma;
   for (int kb = 0; kb <= t.kv_blk; ++kb) {
-    dma.issue(a.kp + ((size_t)bh * a.nblk + kb) * C::KT, a.vp + ((size_t)bh * a.nkb + kb) * C::VT, tiles,
-              tiles + C::KT);
+    dma.issue(a.kp + ((size_t)bh * a.nblk + kb) * C::KT, a.vp + ((size_t)bh * a.nkb + kb) * C::VT,
+              kTiles, kTiles + C::KT);
     wait_lds_dma();
     __syncthreads();
     const int nvalid = min(kBlock, a.N - kb * kBlock);
     const float sk = a.s_k[(size_t)bh * a.nblk + kb];
     if (kb == t.kv_blk)
-      tile_step<D, true>(tiles, tiles + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, &t, wave, a.p_mode);
+      tile_step<D, true>(kTiles, kTiles + C::KT, ptab, qop, cq, a.alpha, sk, nvalid, st, &t, wave, a.pm.P);
     else
-      tile_step<D, false>(tiles, tiles + C::KT, ptab, qop, cq, a.alpha_g, sk, nvalid, st, nullptr, wave, a.p_mode);
+      tile_step<D, false>(kTiles, kTiles + C::KT, ptab, qop, cq, a.alpha, sk, nvalid, st, nullptr, wave, a.pm.P);
     __syncthreads();
   }
 }
 
-// The kernels' P map on grid exponents x <= 0: the same table and index
-// arithmetic, with S = x, c = 1, m = 0 (so v = -x exactly).
-__global__ __launch_bounds__(256) void k_pmap_probe(const float* __restrict__ x, uint8_t* __restrict__ u,
-                                                    int64_t n, int p_mode) {
-  __shared__ __attribute__((aligned(16))) uint8_t tab[kPTabBytes];
-  ptab_build(tab, threadIdx.x, 256, p_mode);
+// The kernels' P map on exponents d: the same table, lookup, marked-cell
+// decision and packing as a step of the attention, with S = d, c = 1 and
+// m = 0 (so x = -d exactly).  Each lane maps 32 consecutive values, as a
+// lane maps its 32 scores of a step; u = code + zero-point.
+__global__ __launch_bounds__(256) void k_pmap_probe(const float* __restrict__ d, uint8_t* __restrict__ u,
+                                                    int64_t n, PMapArgs pm) {
+  __shared__ __attribute__((aligned(16))) uint8_t tab[kPTabBytes + kPThrBytes];
+  ptab_build(tab, threadIdx.x, 256, pm);
   __syncthreads();
+  const int64_t groups = (n + 31) / 32;
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
-    u[i] = (uint8_t)e4m3_to_uint(tab[ptab_addr(x[i], kPTabScale, 0.0f)]);
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups; g += stride) {
+    const int64_t base = g * 32;
+    v16f s[2];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) s[k >> 4][k & 15] = base + k < n ? d[base + k] : 0.0f;
+    uint32_t p[2][4];
+    pmap_codes(s, kPIdxScale, 0.0f, tab, p);
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      if (base + k < n) u[base + k] = (uint8_t)e4m3_to_uint((p[k >> 4][(k & 15) >> 2] >> (8 * (k & 3))) & 0xFFu);
+  }
 }
 
 __global__ void k_copy16(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n16) {
@@ -729,27 +863,32 @@ __global__ void k_copy1(const uint8_t* __restrict__ src, uint8_t* __restrict__ d
   if (i < n) dst[i] = src[i];
 }
 
-void launch_int4_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st) {
-  const unsigned nwg = (unsigned)(B * a.H * ((a.N + kQTile - 1) / kQTile));
+template <int D, bool VH, bool DUMP>
+static void launch_attn_d(const AttnArgs& a, bool out_bf16, unsigned nwg, hipStream_t st) {
   const dim3 blk(64 * kWaves);
+  if (out_bf16) k_int4_attn<D, true, VH, DUMP><<<nwg, blk, 0, st>>>(a);
+  else k_int4_attn<D, false, VH, DUMP><<<nwg, blk, 0, st>>>(a);
+}
+
+template <bool DUMP>
+static void launch_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st) {
+  const unsigned nwg = (unsigned)(B * a.H * ((a.N + kQTile - 1) / kQTile));
   const bool vh = a.v_hadamard != 0;
   if (D == 128) {
-    if (vh) {
-      if (out_bf16) k_int4_attn<128, true, true><<<nwg, blk, 0, st>>>(a);
-      else k_int4_attn<128, false, true><<<nwg, blk, 0, st>>>(a);
-    } else {
-      if (out_bf16) k_int4_attn<128, true, false><<<nwg, blk, 0, st>>>(a);
-      else k_int4_attn<128, false, false><<<nwg, blk, 0, st>>>(a);
-    }
+    if (vh) launch_attn_d<128, true, DUMP>(a, out_bf16, nwg, st);
+    else launch_attn_d<128, false, DUMP>(a, out_bf16, nwg, st);
   } else {
-    if (vh) {
-      if (out_bf16) k_int4_attn<64, true, true><<<nwg, blk, 0, st>>>(a);
-      else k_int4_attn<64, false, true><<<nwg, blk, 0, st>>>(a);
-    } else {
-      if (out_bf16) k_int4_attn<64, true, false><<<nwg, blk, 0, st>>>(a);
-      else k_int4_attn<64, false, false><<<nwg, blk, 0, st>>>(a);
-    }
+    if (vh) launch_attn_d<64, true, DUMP>(a, out_bf16, nwg, st);
+    else launch_attn_d<64, false, DUMP>(a, out_bf16, nwg, st);
   }
+}
+
+void launch_int4_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st) {
+  launch_attn<false>(a, D, out_bf16, B, st);
+}
+
+void launch_int4_attn_rowdbg(const AttnArgs& a, int D, int B, hipStream_t st) {
+  launch_attn<true>(a, D, false, B, st);
 }
 
 void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipStream_t st) {
@@ -757,10 +896,10 @@ void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipS
   else k_int4_tile_dump<64><<<1, 128, 0, st>>>(a, t);
 }
 
-void launch_pmap_probe(const float* x, uint8_t* u, int64_t n, int p_mode, hipStream_t st) {
+void launch_pmap_probe(const float* d, uint8_t* u, int64_t n, const PMapArgs& pm, hipStream_t st) {
   if (n <= 0) return;
-  const int64_t blocks = (n + 255) / 256;
-  k_pmap_probe<<<(unsigned)(blocks < 1024 ? blocks : 1024), 256, 0, st>>>(x, u, n, p_mode);
+  const int64_t blocks = ((n + 31) / 32 + 255) / 256;
+  k_pmap_probe<<<(unsigned)(blocks < 2048 ? blocks : 2048), 256, 0, st>>>(d, u, n, pm);
 }
 
 void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {

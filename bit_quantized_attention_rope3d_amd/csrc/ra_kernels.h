@@ -32,6 +32,21 @@ struct VQuantArgs {
   int N, H, nkb;
 };
 
+// The P map's thresholds as the attention kernels use them ([RA] Sec. 4.2:
+// u = round(P p) with p = 2^d, P = 15 or 7).  With x = -d >= 0, u = #{k :
+// x <= X_k}, X_k the largest binary32 value with P 2^-X_k >= k + 1/2.  The
+// kernels index a byte table by j = rint(x * 4096) (ties to even); cell j
+// is every binary32 x that rounds to j.  cell[k] is the cell holding X_k;
+// bit k of `split` is set when that cell also holds values above X_k (the
+// table then cannot decide, and the kernel compares y = x / 8 with
+// ythr[k] = X_k / 8, both exact).
+struct PMapArgs {
+  int cell[15];
+  float ythr[15];
+  uint32_t split;
+  int P;              // 15 (range-optimized) or 7 (symmetric)
+};
+
 struct AttnArgs {
   const uint8_t* qp;  // Q / K / V code bytes (int4) or bf16 tensors (bf16 path)
   const uint8_t* kp;
@@ -41,10 +56,11 @@ struct AttnArgs {
   const float* s_v;
   void* out;          // [B, N, H, D] f32 or bf16
   int N, H, Npad, nblk, nkb, nqt;
-  float alpha_g;      // f32(log2(e) * softmax_scale * kPGrid)   (int4 path)
-  float alpha;        // f32(log2(e) * softmax_scale)            (bf16 path)
+  float alpha;        // f32(log2(e) * softmax_scale): log2 units per unit of scaled score
   int p_mode;         // 0: range-optimized P (u = round(15 p), code u - 8); 1: symmetric (u = code = round(7 p))
   int v_hadamard;     // V codes are of V H (H = Walsh-Hadamard / sqrt D): the output is multiplied by H
+  PMapArgs pm;        // int4 path
+  uint32_t* row_dbg;  // row fingerprints of the parity variant of the int4 kernel ([B*H*N][4]), else null
 };
 
 struct TileDumpArgs {
@@ -61,7 +77,8 @@ void launch_bf16_prologue(const QKPrologueArgs& qa, const VQuantArgs& vq, int D,
                           hipStream_t st);
 void launch_int4_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
 void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipStream_t st);
-void launch_pmap_probe(const float* x, uint8_t* u, int64_t n, int p_mode, hipStream_t st);
+void launch_int4_attn_rowdbg(const AttnArgs& a, int D, int B, hipStream_t st);
+void launch_pmap_probe(const float* d, uint8_t* u, int64_t n, const PMapArgs& pm, hipStream_t st);
 void launch_bf16_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
 void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 

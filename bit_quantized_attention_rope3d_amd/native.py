@@ -62,7 +62,9 @@ _SIGS = {
     "ra_schedule_pick": (c_i32, [ctypes.POINTER(RaSchedule), c_i32, c_i32, c_i32, c_i32]),
     "ra_status_str": (ctypes.c_char_p, [c_i32]),
     "ra_last_error_message": (ctypes.c_char_p, []),
-    "ra_pgrid": (c_i32, []),
+    "ra_plan_upload": (c_i32, [c_void]),
+    "ra_pmap_thresholds": (c_i32, [c_i32, c_void]),
+    "ra_debug_row_digests": (c_i32, [c_void, c_void, c_void, c_size, c_void, c_void]),
     "ra_debug_prologue": (c_i32, [c_void, c_void, c_void, c_void, c_void, c_size,
                                   c_void, c_void, c_void, c_void, c_void, c_void, c_void]),
     "ra_debug_tile": (c_i32, [c_void, c_void, c_size, c_i32, c_i32, c_i32, c_i32,

@@ -25,7 +25,11 @@
  *   * All device pointers must be 16-byte aligned.
  *   * The caller owns q, k, v, o and the workspace; the library never frees
  *     them.  A plan owns only its RoPE tables (host copy, plus one small
- *     device copy per GPU made on first use).
+ *     device copy per GPU, made by ra_plan_create on the device current then
+ *     and by ra_plan_upload on any other).  The forward entry points
+ *     (ra_attn_fwd, ra_attn_prologue, ra_attn_main, ra_attn_fwd_simple once
+ *     its plan exists) allocate nothing and never synchronise with the
+ *     host, so they may be captured into a HIP graph.
  *   * Every entry point validates its arguments before enqueueing anything and
  *     returns a status; on failure nothing is enqueued and
  *     ra_last_error_message() (thread-local) says why.  Work is enqueued
@@ -79,7 +83,7 @@ typedef struct {
 
 /* Options.  rope_theta: RoPE base (10000 in the pages' models; > 0).
  * softmax_scale: 0 selects 1/sqrt(head_dim).  p_mode selects the INT4 map of
- * the attention probabilities p in [0, 1] ([RA] Sec. 4.2): 0 = range-optimized
+ * the attention probabilities p in [0, 1] (Sec. 4.2): 0 = range-optimized
  * (default; code = round(15 p) - 8, the full signed range [-8, 7]), 1 =
  * symmetric quantization, the baseline the pages improve on (code = round(7 p)
  * in [0, 7], half of the codes unused); other values return
@@ -109,28 +113,36 @@ typedef struct ra_plan_s* ra_plan;
  * theta 10000, scale 1/sqrt(D), range-optimized P. */
 ra_status ra_opts_default(ra_opts* opts);
 
-/* Validate shape/opts and build the RoPE cos/sin tables on the host (binary64
+/* Validate shape/opts, build the RoPE cos/sin tables on the host (binary64
  * angles, +pi/4 per pair for the merged Interleaved rotation, rounded to
- * binary32).  No device work.  *out receives a plan to be destroyed with
+ * binary32) and the P map's thresholds (Sec. 4.2), and, when a GPU is
+ * present, copy the tables to the current device (one small allocation and
+ * a synchronous copy; RA_ERR_OOM / RA_ERR_HIP if that fails, and then no
+ * plan is returned).  *out receives a plan to be destroyed with
  * ra_plan_destroy. */
 ra_status ra_plan_create(const ra_shape* shape, const ra_opts* opts, ra_plan* out);
+
+/* Copy the plan's tables to the current device if they are not there yet
+ * (allocates and synchronises; call it before using the plan on a device
+ * other than the one current at ra_plan_create). */
+ra_status ra_plan_upload(ra_plan plan);
 
 /* Release the plan and its device table copies.  Null is accepted. */
 ra_status ra_plan_destroy(ra_plan plan);
 
 /* Workspace bytes one ra_attn_fwd call of this plan needs (the INT4 codes
- * of Q/K/V in the matrix-instruction operand formats: Q and K as 6-bit fp6
- * e2m3 in 64-token tiles, V as one fp8 e4m3 byte each; + scales; or the bf16
- * copies for the bf16 path). */
+ * of Q/K/V in the matrix-instruction operand format fp6 e2m3, 6 bits per
+ * code, in 64-token tiles: 48 * D bytes per tile of each of Q, K and V; the
+ * scales; or the bf16 copies for the bf16 path). */
 ra_status ra_plan_workspace_size(ra_plan plan, size_t* bytes);
 
 /* Same figure without a plan. */
 ra_status ra_workspace_size(const ra_shape* shape, const ra_opts* opts, size_t* bytes);
 
-/* o = attention(q, k, v) for the plan's shape and options; enqueue only.
- * Equivalent to ra_attn_prologue followed by ra_attn_main on the same
- * workspace.  The first call on a device copies the plan's tables there
- * (one small synchronous allocation + copy). */
+/* o = attention(q, k, v) for the plan's shape and options; enqueue only (no
+ * allocation, no host synchronisation).  Equivalent to ra_attn_prologue
+ * followed by ra_attn_main on the same workspace.  RA_ERR_INVALID_ARG if the
+ * plan's tables are not on the current device (see ra_plan_upload). */
 ra_status ra_attn_fwd(ra_plan plan, const void* q, const void* k, const void* v, void* o,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -144,7 +156,9 @@ ra_status ra_attn_main(ra_plan plan, void* o, void* workspace, size_t workspace_
                        hipStream_t stream);
 
 /* One-shot form: builds (and caches, under a mutex) a plan for these
- * arguments with theta 10000 and scale 1/sqrt(D), then runs ra_attn_fwd. */
+ * arguments with theta 10000 and scale 1/sqrt(D), then runs ra_attn_fwd.
+ * The first call with new arguments creates the plan (and so allocates and
+ * synchronises once); later calls with the same arguments do not. */
 ra_status ra_attn_fwd_simple(const void* q, const void* k, const void* v, void* o,
                              int32_t batch, int32_t heads, int32_t head_dim,
                              int32_t grid_f, int32_t grid_h, int32_t grid_w,
@@ -162,8 +176,12 @@ ra_prec ra_schedule_pick(const ra_schedule* sched, int32_t step, int32_t n_steps
 const char* ra_status_str(ra_status status);
 const char* ra_last_error_message(void);
 
-/* Steps per log2 unit of the grid on which the P exponent is rounded. */
-int32_t ra_pgrid(void);
+/* The P map's thresholds (Sec. 4.2: u = round(P p), p = 2^d, rounded
+ * half up; P = 15 for p_mode 0, 7 for p_mode 1): T[k], k = 0..P-1, the
+ * smallest binary32 d with P 2^d >= k + 1/2, so that u = #{k : d >= T[k]}.
+ * T (host) receives P floats.  p_mode outside {0, 1} or a null T returns
+ * RA_ERR_INVALID_ARG.  Host only. */
+ra_status ra_pmap_thresholds(int32_t p_mode, float* T);
 
 /* ---- parity / diagnostics exports (synchronous, test use) ---------------- */
 
@@ -179,18 +197,33 @@ ra_status ra_debug_prologue(ra_plan plan, const void* q, const void* k, const vo
  * step code for the 64 queries of Q block q_blk of head (b, h) up to key step
  * kv_blk and copy that step's exact integers to host buffers:
  * s_int [64, 64] (query, key) scores, p_codes [64, 64] P codes in [-8, 7]
- * (-8 for keys past N), pv_int [64, D] = sum_j code * vhat, m_after [64] the
- * running max (grid units) after the step.  Rows past N are unspecified. */
+ * (-8 for keys past N; [0, 7] and 0 for p_mode 1), pv_int [64, D] =
+ * sum_j code * vhat, m_after [64] the running max (log2 units, binary32)
+ * after the step.  Rows past N are unspecified. */
 ra_status ra_debug_tile(ra_plan plan, void* workspace, size_t workspace_bytes,
                         int32_t b, int32_t h, int32_t q_blk, int32_t kv_blk,
                         int32_t* s_int, int8_t* p_codes, int32_t* pv_int, float* m_after,
                         hipStream_t stream);
 
-/* Evaluate the kernels' P map of mode p_mode (see ra_opts) on n grid
- * exponents: x (device, f32) -> u (device, u8): u = code + 8 in [0, 15] for
- * p_mode 0, u = code in [0, 7] for p_mode 1.  p_mode outside {0, 1} returns
- * RA_ERR_INVALID_ARG.  Enqueue only. */
-ra_status ra_debug_pmap(const float* x, uint8_t* u, int64_t n, int32_t p_mode, hipStream_t stream);
+/* Evaluate the attention kernels' P map of mode p_mode (see ra_opts) --
+ * their table lookup, exact decision of the table cells that hold a
+ * rounding boundary, and operand packing -- on n exponents d (device, f32,
+ * d = log2 p <= 0) -> u (device, u8): u = round(15 2^d) = code + 8 for
+ * p_mode 0, u = round(7 2^d) = code for p_mode 1.  p_mode outside {0, 1}
+ * returns RA_ERR_INVALID_ARG.  Enqueue only. */
+ra_status ra_debug_pmap(const float* d, uint8_t* u, int64_t n, int32_t p_mode, hipStream_t stream);
+
+/* Stage 2 of an INT4 plan with f32 output (workspace filled by stage 1), run
+ * by the parity variant of the attention kernel: the same kernel, launch
+ * shape, LDS pipeline and step order, which also writes for every query row
+ * r = (b * H + h) * N + n, into rows[4 r .. 4 r + 3] (device, uint32, 16-byte
+ * aligned, B * H * N * 4 entries): the bits of the final running max (log2
+ * units), the sum over all keys of u = code + zero-point, the sum of
+ * u * (2654435761 (j + 1) mod 2^32) mod 2^32 over keys j, and the bits of
+ * the row's final binary32 sum of u (rescaled, as the kernel keeps it).  o
+ * receives the output as ra_attn_main would.  Enqueue only; for tests. */
+ra_status ra_debug_row_digests(ra_plan plan, void* o, void* workspace, size_t workspace_bytes,
+                               uint32_t* rows, hipStream_t stream);
 
 /* Host copy of the plan's binary32 RoPE table of segment `seg` (0 frame,
  * 1 height, 2 width): cos and sin, each [positions, seg_len/2]. */

@@ -133,11 +133,17 @@ def test_calls_reject_bad_buffers_before_device_work(L):
 
 @pytest.mark.parametrize("what,code", [("alloc", "RA_ERR_OOM"), ("launch", "RA_ERR_HIP")])
 def test_fault_injection(L, monkeypatch, what, code):
+    """The table upload (ra_plan_upload; ra_plan_create on a GPU) maps an
+    allocation failure to RA_ERR_OOM, the forward a launch failure to
+    RA_ERR_HIP."""
     from bit_quantized_attention_rope3d_amd.api import Plan
     p = Plan(1, 2, 64, (2, 4, 4), (24, 20, 20))
     a16 = ctypes.c_void_p(0x10000)
     monkeypatch.setenv("RA_FAULT_INJECT", what)
-    rc = native.lib().ra_attn_fwd(p._h, a16, a16, a16, a16, a16, p.workspace_bytes, None)
+    if what == "alloc":
+        rc = native.lib().ra_plan_upload(p._h)
+    else:
+        rc = native.lib().ra_attn_fwd(p._h, a16, a16, a16, a16, a16, p.workspace_bytes, None)
     assert native.STATUS[rc] == code
     assert what in native.last_error()
     p.close()
@@ -165,8 +171,44 @@ def test_schedule_agrees_with_oracle(L, ora):
                     ora.schedule_full_precision(sched, s, 12, b, 9)
 
 
-def test_pgrid_agrees_with_oracle(L, ora):
-    assert native.lib().ra_pgrid() == ora.pgrid()
+@pytest.mark.parametrize("p_mode", [0, 1])
+def test_pmap_thresholds_agree_with_oracle(L, ora, p_mode):
+    """The library finds the P map's thresholds its own way (bisection over
+    binary32 bit patterns); they equal the oracle's (pinned against 40-digit
+    decimal in test_oracle_pmap.py) bit for bit."""
+    from bit_quantized_attention_rope3d_amd.api import pmap_thresholds
+    got = pmap_thresholds(p_mode)
+    want = ora.pmap_thresholds(p_mode)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert native.STATUS[L.ra_pmap_thresholds(2, ctypes.c_void_p(0x10000))] == "RA_ERR_INVALID_ARG"
+    assert native.STATUS[L.ra_pmap_thresholds(0, None)] == "RA_ERR_INVALID_ARG"
+
+
+def test_python_wrappers_reject_bad_tensors(L):
+    """The binding checks every buffer it hands to a kernel: inputs, output
+    and workspace (shape, dtype, contiguity, device), and the one-shot form
+    checks k and v against q, before any call into the library."""
+    import torch
+    from bit_quantized_attention_rope3d_amd.api import Plan, attn_fwd
+    p = Plan(1, 2, 64, (2, 4, 4), (24, 20, 20), in_dtype="f32", out_dtype="f32")
+    q = torch.zeros(p.io_shape, dtype=torch.float32)
+    with pytest.raises(ValueError, match="input must be"):
+        p.forward(q, q, q)                                          # not on a GPU
+    with pytest.raises(ValueError, match="out must be"):
+        p._check_out(torch.zeros(p.io_shape, dtype=torch.bfloat16), q.device)
+    with pytest.raises(ValueError, match="out must be"):
+        p._check_out(torch.zeros((1, 31, 2, 64), dtype=torch.float32), q.device)
+    with pytest.raises(ValueError, match="out must be"):
+        p._check_out(torch.zeros((1, 2, 32, 64), dtype=torch.float32).transpose(1, 2), q.device)
+    with pytest.raises(ValueError, match="workspace must be"):
+        p._ws(torch.zeros(p.workspace_bytes, dtype=torch.int8), q.device)
+    with pytest.raises(ValueError, match="k must be"):
+        attn_fwd(q, q[:, :31], q, (2, 4, 4), (24, 20, 20))
+    with pytest.raises(ValueError, match="v must be"):
+        attn_fwd(q, q, q.to(torch.bfloat16), (2, 4, 4), (24, 20, 20))
+    with pytest.raises(ValueError, match="must be bfloat16 or float32"):
+        attn_fwd(q.double(), q, q, (2, 4, 4), (24, 20, 20))
+    p.close()
 
 
 def test_mfma_peak_probe_validates_before_launch(L):

@@ -6,13 +6,14 @@ range-optimized vs symmetric P, V-side Hadamard, and the bf16 fallback.
 Per workload, 4 heads x 64 query rows (the first block, two interior blocks
 and the ragged tail) of every variant are compared with
   * the oracle's binary64 float path of the same variant (INT4 variants;
-    gated: max-abs 2e-3, cosine 0.999), and
+    gated: max-abs 1e-5), and
   * exact fp64 attention softmax(RoPE(q) RoPE(k)^T / sqrt(D)) v of the
     unrounded inputs (reported, not gated: this is the method's own error).
 Inputs are drawn on the device (torch Philox, the workload's seed) with the
 workload's outlier recipe; two more draws of the Wan-like 720p shape show the
 regimes around it: no outlier channels, and outliers scaled by U[3, 5]
-instead of U[10, 30].  Runs with RA_ACCURACY=1 (under a minute).
+instead of U[10, 30].  The Wan-like 720p workload (the benchmarked one) runs
+by default; the others run with RA_ACCURACY=1 (under a minute each).
 """
 import json
 import os
@@ -24,11 +25,10 @@ import torch
 from bit_quantized_attention_rope3d_amd import inputs
 from oracle import ref_fp64
 
-from gpu_helpers import cosine, plan_for, say
+from gpu_helpers import OUT_TOL, cosine, plan_for, say
 
-pytestmark = [pytest.mark.gpu,
-              pytest.mark.skipif(os.environ.get("RA_ACCURACY") != "1",
-                                 reason="full-size accuracy table runs with RA_ACCURACY=1")]
+pytestmark = pytest.mark.gpu
+FULL = os.environ.get("RA_ACCURACY") == "1"
 
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
@@ -64,8 +64,10 @@ def _workload(name):
     return inputs.get(name)
 
 
-@pytest.mark.parametrize("name", ["wan480", "wan720", "hy720", "wan720_plain", "wan720_mild"])
+@pytest.mark.parametrize("name", ["wan720", "wan480", "hy720", "wan720_plain", "wan720_mild"])
 def test_accuracy_table(ora, name):
+    if name != "wan720" and not FULL:
+        pytest.skip("the other workloads' tables run with RA_ACCURACY=1")
     w = _workload(name)
     N, H = w.tokens, w.heads
     say("accuracy %s: drawing inputs" % name)
@@ -108,4 +110,4 @@ def test_accuracy_table(ora, name):
     say("accuracy table " + json.dumps(dict(workload=name, heads=heads, rows=int(rows.size), table=table)))
     for rec in table:
         if "vs_oracle" in rec:
-            assert rec["vs_oracle"]["max"] <= 2e-3 and rec["vs_oracle"]["cos"] >= 0.999, rec
+            assert rec["vs_oracle"]["max"] <= OUT_TOL and rec["vs_oracle"]["cos"] >= 0.999999, rec

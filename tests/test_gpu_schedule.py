@@ -4,15 +4,16 @@ Each call of a denoise-step x transformer-block sweep draws fresh seeded
 tensors on the device, asks ra_schedule_pick for its precision (bf16 when the
 step or the block is in a head/tail set: RotateAttention review, Sec. 5.1, the
 FP16 fallback schedule) and runs that plan.  INT4 calls are compared with the
-oracle's binary64 float path (max-abs 2e-3, cosine 0.999), bf16 calls with
+oracle's binary64 float path (max-abs 1e-5), bf16 calls with
 fp64 attention on the bf16-rounded RoPE'd inputs (the bf16 path's own bar);
 every call's error against exact fp64 attention of the unrounded inputs is
 printed, not gated.  The aggregate attention time over the sweep is printed.
 
-The small sweep runs by default.  The full sweep -- the Wan-like 720p shape
-(B1, H40, D128, 21x45x80 = 75,600 tokens, Half rotation) over 10 steps x 40
-blocks with 2/2 head/tail steps and 4/4 head/tail blocks -- samples one head x
-64 query rows per call and runs only with RA_FULL_SWEEP=1 (a few minutes).
+Both sweeps run by default: a small one that checks every head and row, and
+the full one -- the Wan-like 720p shape (B1, H40, D128, 21x45x80 = 75,600
+tokens, Half rotation) over 10 steps x 40 blocks with 2/2 head/tail steps and
+4/4 head/tail blocks -- which samples one head x 64 query rows per call (about
+five minutes, mostly the CPU checks; progress is printed per step).
 """
 import json
 import os
@@ -26,7 +27,7 @@ import torch
 from bit_quantized_attention_rope3d_amd import inputs
 from oracle import ref_fp64
 
-from gpu_helpers import bf16_round, cosine, plan_for, say
+from gpu_helpers import OUT_TOL, bf16_round, cosine, plan_for, say
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +54,7 @@ def _check_call(ora, w, prec, qh, kh, vh, rows, o):
         pro = ora.prologue(qh, kh, vh, w.grid, w.seg, w.theta, w.rot_id)
         want = ora.attention_rows(pro, 0, 0, rows)
         rec.update(gate="oracle", max=float(np.abs(o - want).max()), cos=cosine(o, want))
-        rec["ok"] = rec["max"] <= 2e-3 and rec["cos"] >= 0.999
+        rec["ok"] = rec["max"] <= OUT_TOL and rec["cos"] >= 0.999999
     else:
         qb = bf16_round(qr.astype(np.float32)).astype(np.float64)
         kb = bf16_round(kr.astype(np.float32)).astype(np.float64)
@@ -99,9 +100,12 @@ def run_sweep(ora, w, n_steps, n_blocks, sched, rows_per_call=None, all_heads=Tr
             torch.cuda.synchronize()
             records.append(dict(step=step, block=block, prec=prec, ms=e0.elapsed_time(e1)))
             del q, k, v
+        done = sum(f.done() for *_, f in futures)
+        say("sweep %s: step %d of %d launched (%d calls, %d of %d checks done)"
+            % (w.name, step + 1, n_steps, len(records), done, len(futures)))
     wall = time.perf_counter() - t_wall
     errs = []
-    for step, block, h, prec, f in futures:
+    for i, (step, block, h, prec, f) in enumerate(futures):
         r = f.result()
         r.update(step=step, block=block, head=h, prec=prec)
         errs.append(r)
@@ -136,8 +140,7 @@ def test_schedule_sweep_small(ora):
     assert s["int4_calls"] == 8 and s["calls"] == 24
 
 
-@pytest.mark.skipif(os.environ.get("RA_FULL_SWEEP") != "1",
-                    reason="full-size sweep (400 calls at 75,600 tokens) runs with RA_FULL_SWEEP=1")
+@pytest.mark.timeout(1200)
 def test_schedule_sweep_wan720(ora):
     w = inputs.get("wan720")
     threads = ora.get_threads()
