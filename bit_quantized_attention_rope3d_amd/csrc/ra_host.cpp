@@ -88,6 +88,11 @@ ra::PMapArgs pmap_args(int p_mode) {
     pm.ythr[k] = xk * 0.125f;
     if (pmap_cell(std::nextafter(xk, INFINITY)) == pm.cell[k]) pm.split |= 1u << k;
   }
+  // The first even cell past X_0's: every x from there on has u = 0.  Even,
+  // so that rint(top - 4096 x), the kernels' reversed address, is exactly
+  // top - rint(4096 x) at ties as well.
+  pm.top = (pm.cell[0] + 2) & ~1;
+  pm.top_sub = std::ldexp((float)pm.top, -149);
   return pm;
 }
 
@@ -339,6 +344,11 @@ ra_status ra_plan_create(const ra_shape* shape, const ra_opts* opts, ra_plan* ou
   const double scale = opts->softmax_scale > 0.0 ? opts->softmax_scale : 1.0 / std::sqrt((double)shape->head_dim);
   p->alpha = (float)(M_LOG2E * scale);
   p->pm = pmap_args(opts->p_mode);
+  if (p->pm.top + 1 > ra::kPTabEntries) {
+    delete p;
+    return fail(RA_ERR_UNSUPPORTED, "P-map table needs %d entries (built for %d)", p->pm.top + 1,
+                ra::kPTabEntries);
+  }
   build_tables(p);
   // Tables go to the current device now, so that the forward calls neither
   // allocate nor synchronise.  With no device present the plan still serves

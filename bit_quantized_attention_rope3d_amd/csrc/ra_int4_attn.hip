@@ -74,28 +74,30 @@ struct State {
 // (PMapArgs).  With c' = c / 8 and m' = m / 8 (exact power-of-two scalings):
 //   y = clamp(fma(S, -c', m'))   f32(m - S c) / 8 = x / 8, clamped to
 //                                [0, 1]: keys at or above the running max
-//                                (d >= 0) give 0, the top code; x >= 8 (no
-//                                code above 0 there) saturates at 1; with
-//                                the DX10 clamp mode of compute kernels a
-//                                NaN or a -0 becomes +0
-//   w = y 2^-134                 subnormal (f32 denormals are enabled in
-//                                these kernels), spacing 2^-149 = 2^-15 of
-//                                y: the product rounds 4096 x to the
-//                                nearest integer, ties to even, and
-//                                bits(w) = j in [0, 2^15]
-// The table sits at LDS address 0, so j is the byte address of its entry.
+//                                (d >= 0) give 0, the top code; with the
+//                                DX10 clamp mode of compute kernels a NaN
+//                                or a -0 becomes +0
+//   w = clamp(fma(y, -2^-134, top 2^-149))
+//                                a subnormal (f32 denormals are enabled in
+//                                these kernels) of spacing 2^-149: the sum
+//                                rounds top - 4096 x to the nearest
+//                                integer, ties to even, and the clamp sends
+//                                every negative result to +0, so
+//                                bits(w) = max(top - rint(4096 x), 0)
+// The table sits at LDS address 0 and bits(w) is the byte address of the
+// entry of cell j = rint(4096 x), stored in reverse: address top - j, and
+// address 0 for every j >= top, where u = 0.  All keys that far below the
+// running max (most keys of a long row) read the same byte, a broadcast.
 // Scalings by 1/8 are exact unless a value is below 2^-123, and then x is
-// far below the smallest X_k and every path gives cell 0 and u = P.  The
-// running max is passed as m' + 0, which turns a -0 into +0.
+// far below the smallest X_k and every path gives u = P.  The running max
+// is passed as m' + 0, which turns a -0 into +0.
 //
-// Entry j is e4m3(u) when every x of cell j has the same u; in the cell of
-// an X_k that also holds values above it, the entry is 0x80 | k (no e4m3
-// code of 0..15 has bit 7 set) and u = k + (y <= X_k / 8), decided by
-// pmap_fix after the lookup from the 8-byte record k behind the table:
-// X_k / 8, then the bytes e4m3(k) and e4m3(k + 1).
-constexpr int kPTabSpan = 1 << 15;
-constexpr int kPTabEntries = kPTabSpan + 1;                 // j = 0..2^15
-constexpr int kPTabBytes = (kPTabEntries + 15) & ~15;       // one byte each, 16-byte padded
+// The entry of cell j is e4m3(u) when every x of the cell has the same u;
+// in the cell of an X_k that also holds values above it, the entry is
+// 0x80 | k (no e4m3 code of 0..15 has bit 7 set) and u = k + (y <= X_k / 8),
+// decided by pmap_fix after the lookup from the 8-byte record k behind the
+// table: X_k / 8, then the bytes e4m3(k) and e4m3(k + 1).
+constexpr int kPTabBytes = (kPTabEntries + 15) & ~15;       // one byte per cell, 16-byte padded
 constexpr int kPThrBytes = 16 * 8;                          // 16 records behind the table
 constexpr float kPIdxScale = 0.125f;                        // 2^-3
 constexpr uint32_t kPSplit = 0x80808080u;                   // marked entries, per packed byte
@@ -105,8 +107,8 @@ __device__ __forceinline__ float pmap_y(float s, float c2, float m2) {
   return __builtin_amdgcn_fmed3f(__builtin_fmaf(s, -c2, m2), 0.0f, 1.0f);
 }
 
-__device__ __forceinline__ uint32_t ptab_addr(float s, float c2, float m2) {
-  return __float_as_uint(pmap_y(s, c2, m2) * 0x1p-134f);
+__device__ __forceinline__ uint32_t ptab_addr(float s, float c2, float m2, float top_sub) {
+  return __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(pmap_y(s, c2, m2), -0x1p-134f, top_sub), 0.0f, 1.0f));
 }
 
 // e4m3 encoding of an integer 0 <= u <= 15 (exact).
@@ -123,19 +125,21 @@ __device__ __forceinline__ uint32_t e4m3_to_uint(uint32_t b) {
   return ((8u | m) << e) >> 3;
 }
 
-// Fill the table and the thresholds behind it cooperatively (threads tid,
-// tid + nt, ...): entry j counts the X_k whose cell lies above j (cell j
-// holds only x below them), plus the X_k whose cell is j when that cell
-// holds nothing above it; a cell that does is marked with its k.
+// Fill the table and the records behind it cooperatively (threads tid,
+// tid + nt, ...): the entry of cell j = top - a counts the X_k whose cell
+// lies above j (cell j holds only x below them), plus the X_k whose cell is
+// j when that cell holds nothing above it; a cell that does is marked with
+// its k.
 __device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt, const PMapArgs& pm) {
-  for (int j = tid; j < kPTabEntries; j += nt) {
+  for (int a = tid; a <= pm.top; a += nt) {
+    const int j = pm.top - a;
     uint32_t u = 0, mark = 0;
     for (int k = 0; k < pm.P; ++k) {
       const bool split = (pm.split >> k) & 1u;
       if (j < pm.cell[k] || (j == pm.cell[k] && !split)) ++u;
       if (j == pm.cell[k] && split) mark = 0x80u | (uint32_t)k;
     }
-    tab[j] = (uint8_t)(mark ? mark : e4m3_of_uint(u));
+    tab[a] = (uint8_t)(mark ? mark : e4m3_of_uint(u));
   }
   uint32_t* rec = reinterpret_cast<uint32_t*>(tab + kPTabBytes);
   for (int k = tid; k < 16; k += nt) {
@@ -147,10 +151,6 @@ __device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt, const 
 // ---- K/V staging: global memory -> LDS without registers ------------------
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-// LDS address (offset in the workgroup's LDS) of a __shared__ location.
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_u8*)p;
-}
 // 16-byte buffer load with the LDS-direct bit: lane i copies 16 bytes from
 // base(rsrc) + voffset into LDS at lds + 16 i (lds is wave-uniform).  It is
 // written as an instruction the compiler does not model as a store to LDS:
@@ -218,7 +218,7 @@ struct TileDma {
   }
 
   // K tile at kt -> kst, V tile at vt -> vst (global addresses of the
-  // tiles, LDS addresses of the stages); a null tile is skipped.
+  // tiles); a null tile is skipped.
   __device__ __forceinline__ void issue(const uint8_t* kt, const uint8_t* vt, uint32_t kst, uint32_t vst) const {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
@@ -258,9 +258,13 @@ __device__ __forceinline__ int acc_key(int mt, int r, int hf) {
 // loop-invariant register per read and re-adds the stage offset to each,
 // instead of one add per base and the constants in the read instructions.
 typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
-__device__ __forceinline__ lds_cu8* lds_base(uint32_t a) {
-  asm("" : "+v"(a));
-  return (lds_cu8*)a;
+__device__ __forceinline__ lds_cu8* lds_base(uint32_t a) { return (lds_cu8*)a; }
+// A stage's LDS address as an opaque scalar: the compiler can neither fold
+// it into the per-lane offsets (one loop-invariant register per unrolled
+// step and operand) nor hoist the one add per operand and step.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
 }
 template <typename T>
 __device__ __forceinline__ T lds_ld(lds_cu8* p) {
@@ -272,24 +276,6 @@ __device__ __forceinline__ T lds_ld(lds_cu8* p) {
 // registers of an fp6 operand must be consecutive).  No instruction.
 __device__ __forceinline__ void operand_fence() { asm volatile("" ::: "memory"); }
 
-// This lane's byte offsets inside a K stage (fp6 K operand: 16-byte and
-// 8-byte part) and a V stage (fp6 V operand), computed once and hidden from
-// the optimizer, so that each step adds the stage address to each of them
-// once and the compiler keeps no further copies of them.
-struct LaneLds {
-  uint32_t klo, khi, vlo, vhi;
-};
-__device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-template <int D>
-__device__ __forceinline__ LaneLds lane_lds() {
-  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
-  return LaneLds{opaque_v((uint32_t)qk6_lo_off(ln, hf)), opaque_v((uint32_t)qk6_hi_off(D, ln, hf)),
-                 opaque_v((uint32_t)v6_lo_off(D, ln, hf)), opaque_v((uint32_t)v6_hi_off(D, ln, hf))};
-}
-
 // ---- building blocks of one 64-key step for the 32 queries of a wave ------
 
 // S^T of the step (exact integers in fp32): kst is the step's fp6 K tile.
@@ -298,9 +284,10 @@ __device__ __forceinline__ LaneLds lane_lds() {
 // addresses (no bank conflicts without a swizzle).  Both offsets are linear
 // in (row, group), so one lane base per part plus constants covers all reads.
 template <int D>
-__device__ __forceinline__ void qk_step(uint32_t kst, const LaneLds& ll, const v8i (&qop)[Cfg<D>::QC], v16f (&s)[2]) {
-  lds_cu8* const klo = lds_base(kst + ll.klo);
-  lds_cu8* const khi = lds_base(kst + ll.khi);
+__device__ __forceinline__ void qk_step(uint32_t kst, const v8i (&qop)[Cfg<D>::QC], v16f (&s)[2]) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
+  lds_cu8* const klo = lds_base(kst + qk6_lo_off(ln, hf));
+  lds_cu8* const khi = lds_base(kst + qk6_hi_off(D, ln, hf));
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -352,11 +339,11 @@ __device__ __forceinline__ float running_max(const v16f (&s)[2], float c, float 
 // paid once per step; each load leaves one byte in the low end of its
 // register, and two v_perm (bytes 0-1 and 2-3) and an OR pack four of them.
 // Marked entries (bit 7) still need pmap_fix.
-__device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c2, float m2, const uint8_t* tab,
-                                          uint32_t (&p)[2][4]) {
+__device__ __forceinline__ void pmap_step(const v16f (&s)[2], float c2, float m2, float top_sub,
+                                          const uint8_t* tab, uint32_t (&p)[2][4]) {
   uint32_t x[32];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) x[k] = tab[ptab_addr(s[k >> 4][k & 15], c2, m2)];
+  for (int k = 0; k < 32; ++k) x[k] = tab[ptab_addr(s[k >> 4][k & 15], c2, m2, top_sub)];
 #pragma unroll
   for (int w = 0; w < 8; ++w)
     p[w >> 2][w & 3] = __builtin_amdgcn_perm(x[4 * w + 1], x[4 * w], 0x0C0C0400u) |
@@ -396,9 +383,9 @@ __device__ __forceinline__ void pmap_fix(const v16f (&s)[2], float c2, float m2,
 
 // The whole P map of a step: lookups, then the exact decision of marked
 // entries when the wave has any (rare: 15 cells of 2^15).
-__device__ __forceinline__ void pmap_codes(const v16f (&s)[2], float c2, float m2, const uint8_t* tab,
-                                           uint32_t (&p)[2][4]) {
-  pmap_step(s, c2, m2, tab, p);
+__device__ __forceinline__ void pmap_codes(const v16f (&s)[2], float c2, float m2, float top_sub,
+                                           const uint8_t* tab, uint32_t (&p)[2][4]) {
+  pmap_step(s, c2, m2, top_sub, tab, p);
   if (__builtin_expect(pmap_marked(p), 0)) pmap_fix(s, c2, m2, tab + kPTabBytes, p);
 }
 
@@ -429,6 +416,15 @@ __device__ __forceinline__ v8i lsum_selector() {
   const int one = 0x22222222;                 // fp4 e2m1 1.0 = 0x2
   return odd ? v8i{0, 0, one, one, 0, 0, 0, 0} : v8i{one, one, 0, 0, 0, 0, 0, 0};
 }
+// The selector rebuilt at its use (two selects), so that it occupies no
+// registers between steps: the main loop has none to spare.
+__device__ __forceinline__ v8i lsum_selector_at_use() {
+  int odd = (threadIdx.x >> 2) & 1;
+  asm volatile("" : "+v"(odd));
+  const int one = 0x22222222;
+  const int a = odd ? 0 : one, b = odd ? one : 0;
+  return v8i{a, a, b, b, 0, 0, 0, 0};
+}
 __device__ __forceinline__ void lsum_step(const v8i& sel, const uint32_t (&p)[2][4], v4f& lsum) {
   const v8i pb = v8i{(int)p[0][0], (int)p[0][1], (int)p[0][2], (int)p[0][3],
                      (int)p[1][0], (int)p[1][1], (int)p[1][2], (int)p[1][3]};
@@ -440,12 +436,13 @@ __device__ __forceinline__ void lsum_step(const v8i& sel, const uint32_t (&p)[2]
 // supplies the fp6 string of channel 32 dt + ln, half hf: one 16-byte and
 // one 8-byte read, tile dt 512 and 256 bytes past the lane bases.
 template <int D>
-__device__ __forceinline__ void pv_step(uint32_t vst, const LaneLds& ll, const uint32_t (&p)[2][4],
+__device__ __forceinline__ void pv_step(uint32_t vst, const uint32_t (&p)[2][4],
                                         v16f (&acc)[Cfg<D>::DT]) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const v8i pb = v8i{(int)p[0][0], (int)p[0][1], (int)p[0][2], (int)p[0][3],
                      (int)p[1][0], (int)p[1][1], (int)p[1][2], (int)p[1][3]};
-  lds_cu8* const vlo = lds_base(vst + ll.vlo);
-  lds_cu8* const vhi = lds_base(vst + ll.vhi);
+  lds_cu8* const vlo = lds_base(vst + v6_lo_off(D, ln, hf));
+  lds_cu8* const vhi = lds_base(vst + v6_hi_off(D, ln, hf));
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
     const v4i lo = lds_ld<v4i>(vlo + 512 * dt);
@@ -480,22 +477,21 @@ template <int D, bool DUMP>
 __device__ __forceinline__ void tile_step(uint32_t kst, uint32_t vst, const uint8_t* tab,
                                           const v8i (&qop)[Cfg<D>::QC], float cq, float alpha,
                                           float sk, int nvalid, State<D>& st,
-                                          const TileDumpArgs* dump, int wave, int P) {
+                                          const TileDumpArgs* dump, int wave, int P, float top_sub) {
   const int zp = P == 15 ? 8 : 0;                  // code = u - zp
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   v16f s[2];
-  const LaneLds ll = lane_lds<D>();
-  qk_step<D>(kst, ll, qop, s);
+  qk_step<D>(kst, qop, s);
   if (nvalid < kBlock) mask_scores(s, nvalid);
   const float cp = score_scale(cq, sk, alpha);
   const float m_new = running_max(s, cp, st.m);
   if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
   st.m = m_new;
   uint32_t p[2][4];
-  pmap_codes(s, cp * kPIdxScale, m_new * kPIdxScale + 0.0f, tab, p);
+  pmap_codes(s, cp * kPIdxScale, m_new * kPIdxScale + 0.0f, top_sub, tab, p);
   if (nvalid < kBlock) mask_p(p, nvalid);
-  pv_step<D>(vst, ll, p, st.acc);
+  pv_step<D>(vst, p, st.acc);
   lsum_step(lsum_selector(), p, st.lsum);
 
   if (DUMP) {
@@ -520,8 +516,8 @@ __device__ __forceinline__ void tile_step(uint32_t kst, uint32_t vst, const uint
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) { pv[dt][r] = 0.0f; cs[dt][r] = 0.0f; }
-    pv_step<D>(vst, ll, p, pv);
-    pv_step<D>(vst, ll, ones, cs);
+    pv_step<D>(vst, p, pv);
+    pv_step<D>(vst, ones, cs);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -620,7 +616,8 @@ template <int D, bool OUT_BF16, bool VH, bool DUMP>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPTabBytes + kPThrBytes + kStages * (C::KT + C::VT)];
-  uint8_t* const ptab = smem;                               // P-map table at LDS address 0, then K and V stages
+  uint8_t* const ptab = smem;                               // P-map table at LDS address 0
+
   ptab_build(ptab, threadIdx.x, 64 * kWaves, a.pm);         // visible after the first barrier
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
@@ -649,7 +646,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
 
   State<D> st;
   state_init<D>(st);
-  const v8i lsel = lsum_selector();
   uint32_t dsum = 0, dhash = 0;                             // DUMP only
 
   // Step t: P codes of step t (S in registers), S of step t+1, P x V of step
@@ -667,10 +663,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   const uint8_t* const ktiles = a.kp + (size_t)bh * a.nblk * C::KT;
   const uint8_t* const vtiles = a.vp + (size_t)bh * a.nkb * C::VT;
   // smem is the kernel's only LDS variable, at LDS address 0 (the P-map
-  // lookup relies on it), so the stages' LDS addresses are constants.
+  // lookup relies on it): K stages follow the table, then the V stages.
   constexpr uint32_t kbase = kPTabBytes + kPThrBytes, vbase = kbase + kStages * C::KT;
-  auto kst = [&](int t) { return kbase + (uint32_t)((t % kStages) * C::KT); };
-  auto vst = [&](int t) { return vbase + (uint32_t)((t % kStages) * C::VT); };
+  auto kst = [&](int t) { return opaque_s(kbase + (uint32_t)((t % kStages) * C::KT)); };
+  auto vst = [&](int t) { return opaque_s(vbase + (uint32_t)((t % kStages) * C::VT)); };
   dma.issue(ktiles, nullptr, kst(0), vst(0));
   wait_lds_dma();
   __syncthreads();
@@ -679,8 +675,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     dma.issue(i < nkb ? ktiles + i * C::KT : nullptr, i - 1 < nkb ? vtiles + (i - 1) * C::VT : nullptr,
               kst(i), vst(i - 1));
   v16f s[2];
-  const LaneLds ll = lane_lds<D>();
-  qk_step<D>(kst(0), ll, qop, s);
+  qk_step<D>(kst(0), qop, s);
   {
     const int nv0 = min(kBlock, a.N);
     if (nv0 < kBlock) mask_scores(s, nv0);
@@ -696,11 +691,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     dma.issue(t + kSync + 1 < nkb ? ktn : nullptr, t + kSync < nkb ? vtn : nullptr, kst(t + kSync + 1),
               vst(t + kSync));
     uint32_t p[2][4];
-    pmap_codes(s, cp_cur * kPIdxScale, st.m * kPIdxScale + 0.0f, ptab, p);
+    pmap_codes(s, cp_cur * kPIdxScale, st.m * kPIdxScale + 0.0f, a.pm.top_sub, ptab, p);
     if constexpr (DUMP) row_digest(p, t, dsum, dhash);
-    qk_step<D>(kst(t + 1), ll, qop, s);   // S of step t+1
-    pv_step<D>(vst(t), ll, p, st.acc);
-    lsum_step(lsel, p, st.lsum);
+    qk_step<D>(kst(t + 1), qop, s);       // S of step t+1
+    pv_step<D>(vst(t), p, st.acc);
+    lsum_step(lsum_selector_at_use(), p, st.lsum);
     if constexpr (decltype(ragged)::value) {
       const int nv1 = a.N - (t + 1) * kBlock;
       if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
@@ -732,11 +727,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     // The last step: its V tile is resident since the barrier before it.
     const int t = nkb - 1, nvalid = a.N - t * kBlock;
     uint32_t p[2][4];
-    pmap_codes(s, cp_cur * kPIdxScale, st.m * kPIdxScale + 0.0f, ptab, p);
+    pmap_codes(s, cp_cur * kPIdxScale, st.m * kPIdxScale + 0.0f, a.pm.top_sub, ptab, p);
     if (nvalid < kBlock) mask_p(p, nvalid);
     if constexpr (DUMP) row_digest(p, t, dsum, dhash);
-    pv_step<D>(vst(t), ll, p, st.acc);
-    lsum_step(lsel, p, st.lsum);
+    pv_step<D>(vst(t), p, st.acc);
+    lsum_step(lsum_selector_at_use(), p, st.lsum);
   }
 
   if constexpr (DUMP) {
@@ -802,7 +797,7 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPTabBytes + kPThrBytes + C::KT + C::VT];
   uint8_t* const ptab = smem;
-  constexpr uint32_t kTiles = kPTabBytes + kPThrBytes;     // LDS address of the K tile, then V
+  constexpr uint32_t tiles = kPTabBytes + kPThrBytes;      // LDS address of the K tile, then the V tile
   ptab_build(ptab, threadIdx.x, 128, a.pm);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const int bh = t.bh;
@@ -814,16 +809,16 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   state_init<D>(st);
   const TileDma<D, 2> dma;
   for (int kb = 0; kb <= t.kv_blk; ++kb) {
-    dma.issue(a.kp + ((size_t)bh * a.nblk + kb) * C::KT, a.vp + ((size_t)bh * a.nkb + kb) * C::VT,
-              kTiles, kTiles + C::KT);
+    dma.issue(a.kp + ((size_t)bh * a.nblk + kb) * C::KT, a.vp + ((size_t)bh * a.nkb + kb) * C::VT, tiles,
+              tiles + C::KT);
     wait_lds_dma();
     __syncthreads();
     const int nvalid = min(kBlock, a.N - kb * kBlock);
     const float sk = a.s_k[(size_t)bh * a.nblk + kb];
     if (kb == t.kv_blk)
-      tile_step<D, true>(kTiles, kTiles + C::KT, ptab, qop, cq, a.alpha, sk, nvalid, st, &t, wave, a.pm.P);
+      tile_step<D, true>(tiles, tiles + C::KT, ptab, qop, cq, a.alpha, sk, nvalid, st, &t, wave, a.pm.P, a.pm.top_sub);
     else
-      tile_step<D, false>(kTiles, kTiles + C::KT, ptab, qop, cq, a.alpha, sk, nvalid, st, nullptr, wave, a.pm.P);
+      tile_step<D, false>(tiles, tiles + C::KT, ptab, qop, cq, a.alpha, sk, nvalid, st, nullptr, wave, a.pm.P, a.pm.top_sub);
     __syncthreads();
   }
 }
@@ -845,7 +840,7 @@ __global__ __launch_bounds__(256) void k_pmap_probe(const float* __restrict__ d,
 #pragma unroll
     for (int k = 0; k < 32; ++k) s[k >> 4][k & 15] = base + k < n ? d[base + k] : 0.0f;
     uint32_t p[2][4];
-    pmap_codes(s, kPIdxScale, 0.0f, tab, p);
+    pmap_codes(s, kPIdxScale, 0.0f, pm.top_sub, tab, p);
 #pragma unroll
     for (int k = 0; k < 32; ++k)
       if (base + k < n) u[base + k] = (uint8_t)e4m3_to_uint((p[k >> 4][(k & 15) >> 2] >> (8 * (k & 3))) & 0xFFu);

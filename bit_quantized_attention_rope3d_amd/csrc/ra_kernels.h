@@ -35,16 +35,20 @@ struct VQuantArgs {
 // The P map's thresholds as the attention kernels use them ([RA] Sec. 4.2:
 // u = round(P p) with p = 2^d, P = 15 or 7).  With x = -d >= 0, u = #{k :
 // x <= X_k}, X_k the largest binary32 value with P 2^-X_k >= k + 1/2.  The
-// kernels index a byte table by j = rint(x * 4096) (ties to even); cell j
-// is every binary32 x that rounds to j.  cell[k] is the cell holding X_k;
-// bit k of `split` is set when that cell also holds values above X_k (the
-// table then cannot decide, and the kernel compares y = x / 8 with
-// ythr[k] = X_k / 8, both exact).
+// kernels sort x into cells j = rint(x * 4096) (ties to even) and keep one
+// byte per cell in a table, stored in reverse at address top - j, with
+// every j >= top (no code above 0 there) at address 0.  cell[k] is the
+// cell holding X_k; bit k of `split` is set when that cell also holds
+// values above X_k (the table then cannot decide, and the kernel compares
+// y = x / 8 with ythr[k] = X_k / 8, both exact).
+constexpr int kPTabEntries = 20112;   // table bytes: top + 1 <= this for P = 15 and 7
 struct PMapArgs {
   int cell[15];
   float ythr[15];
   uint32_t split;
   int P;              // 15 (range-optimized) or 7 (symmetric)
+  int top;            // even, above cell[0]
+  float top_sub;      // top * 2^-149 (a binary32 subnormal)
 };
 
 struct AttnArgs {
