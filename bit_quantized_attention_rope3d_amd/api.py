@@ -112,6 +112,17 @@ class Plan:
 
     __call__ = forward
 
+    def forward_noalloc(self, q, k, v, out=None, stream=None):
+        """ra_attn_fwd_noalloc: the same forward with the library's fixed
+        device-resident workspace (for plans of at most
+        RA_NOALLOC_WORKSPACE_BYTES; calls on one GPU share it)."""
+        self._check_in(q, k, v)
+        out = self.empty_out(q.device) if out is None else out
+        self._check_out(out, q.device)
+        check(lib().ra_attn_fwd_noalloc(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                        _stream_ptr(stream, q.device)), "ra_attn_fwd_noalloc")
+        return out
+
     def prologue(self, q, k, v, workspace, stream=None):
         self._check_in(q, k, v)
         workspace = self._ws(workspace, q.device)

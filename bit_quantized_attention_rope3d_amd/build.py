@@ -26,7 +26,8 @@ LIB = os.path.join(PKG, "libra_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["ra_host.cpp", "ra_prologue.hip", "ra_int4_attn.hip", "ra_bf16_attn.hip", "ra_peak.hip"]
+SOURCES = ["ra_host.cpp", "ra_prologue.hip", "ra_int4_attn.hip", "ra_bf16_attn.hip", "ra_peak.hip",
+           "ra_noalloc.hip"]
 EXTRA = {"ra_int4_attn.hip": ["-fno-honor-nans"]}
 
 CFLAGS = [

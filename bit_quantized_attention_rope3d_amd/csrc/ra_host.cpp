@@ -364,6 +364,8 @@ ra_status ra_plan_create(const ra_shape* shape, const ra_opts* opts, ra_plan* ou
       delete p;
       return st;
     }
+    void* ws = nullptr;   // resolve the no-allocation workspace of this device now
+    if (ra::noalloc_scratch(&ws) != hipSuccess) (void)hipGetLastError();
   }
   *out = p;
   return ok();
@@ -478,6 +480,21 @@ ra_status ra_attn_fwd(ra_plan p, const void* q, const void* k, const void* v, vo
   ra_status st = ra_attn_prologue(p, q, k, v, ws, ws_bytes, stream);
   if (st != RA_OK) return st;
   return ra_attn_main(p, o, ws, ws_bytes, stream);
+}
+
+ra_status ra_attn_fwd_noalloc(ra_plan p, const void* q, const void* k, const void* v, void* o,
+                              hipStream_t stream) {
+  if (!p) return fail(RA_ERR_INVALID_ARG, "plan is null");
+  if (p->lay.total > (size_t)RA_NOALLOC_WORKSPACE_BYTES)
+    return fail(RA_ERR_WORKSPACE,
+                "this plan needs a %zu-byte workspace; the no-allocation entry point holds at most %zu "
+                "bytes (use ra_attn_fwd with a caller workspace)",
+                p->lay.total, (size_t)RA_NOALLOC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  const hipError_t e = ra::noalloc_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(RA_ERR_HIP, "looking up the device workspace failed: %s", hipGetErrorString(e));
+  return ra_attn_fwd(p, q, k, v, o, ws, (size_t)RA_NOALLOC_WORKSPACE_BYTES, stream);
 }
 
 ra_status ra_attn_fwd_simple(const void* q, const void* k, const void* v, void* o, int32_t batch,

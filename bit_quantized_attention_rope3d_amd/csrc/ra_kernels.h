@@ -86,6 +86,10 @@ void launch_pmap_probe(const float* d, uint8_t* u, int64_t n, const PMapArgs& pm
 void launch_bf16_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
 void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 
+// Device address of the current device's no-allocation workspace
+// (ra_noalloc.hip).
+hipError_t noalloc_scratch(void** ptr);
+
 // Operand types of the matrix-core throughput kernel (ra_peak.hip).
 enum PeakKind { kPeakI8 = 0, kPeakFp8 = 1, kPeakFp6 = 2, kPeakFp6Fp8 = 3, kPeakBf16 = 4 };
 void launch_mfma_peak(int kind, int iters, int blocks, float* sink, uint64_t* clk, hipStream_t st);

@@ -58,6 +58,7 @@ _SIGS = {
     "ra_attn_fwd": (c_i32, [c_void, c_void, c_void, c_void, c_void, c_void, c_size, c_void]),
     "ra_attn_prologue": (c_i32, [c_void, c_void, c_void, c_void, c_void, c_size, c_void]),
     "ra_attn_main": (c_i32, [c_void, c_void, c_void, c_size, c_void]),
+    "ra_attn_fwd_noalloc": (c_i32, [c_void, c_void, c_void, c_void, c_void, c_void]),
     "ra_attn_fwd_simple": (c_i32, [c_void, c_void, c_void, c_void] + [c_i32] * 13 + [c_void, c_size, c_void]),
     "ra_schedule_pick": (c_i32, [ctypes.POINTER(RaSchedule), c_i32, c_i32, c_i32, c_i32]),
     "ra_status_str": (ctypes.c_char_p, [c_i32]),

@@ -146,6 +146,25 @@ ra_status ra_workspace_size(const ra_shape* shape, const ra_opts* opts, size_t* 
 ra_status ra_attn_fwd(ra_plan plan, const void* q, const void* k, const void* v, void* o,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the device-resident workspace of ra_attn_fwd_noalloc (one copy
+ * per GPU, held until the process ends). */
+#define RA_NOALLOC_WORKSPACE_BYTES (64u << 20)
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): ra_attn_fwd with the
+ * workspace taken from a fixed device-resident array of
+ * RA_NOALLOC_WORKSPACE_BYTES per GPU instead of a caller buffer.  Same
+ * kernels and results as ra_attn_fwd.  The caller still passes q, k, v and
+ * o.  A plan whose workspace (ra_plan_workspace_size) exceeds
+ * RA_NOALLOC_WORKSPACE_BYTES returns RA_ERR_WORKSPACE and enqueues nothing.
+ * Allocates nothing; the first call on a device without a plan created
+ * there looks the array's address up (no allocation).  Every call on one
+ * GPU shares that GPU's array, which keeps the last call's contents: calls
+ * that overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller.  Enqueue only. */
+ra_status ra_attn_fwd_noalloc(ra_plan plan, const void* q, const void* k, const void* v, void* o,
+                              hipStream_t stream);
+
 /* Stage 1: RoPE + rotation + quantization (INT4) or RoPE + bf16 conversion
  * (bf16 path) of q, k, v into the workspace. */
 ra_status ra_attn_prologue(ra_plan plan, const void* q, const void* k, const void* v,
