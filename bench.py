@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-accuracy", action="store_true",
+                    help="skip the error of sampled rows against the oracle and fp64 attention")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip the sustained MFMA throughput probe")
@@ -198,6 +200,94 @@ def cpu_baseline(w, q, k, v, gpu_out, target_s):
         parity_rows=dict(rows=int(rows.size), max_abs_vs_gpu=diff, cosine_vs_gpu=cos))
 
 
+def cpu_model():
+    """The host CPU's model name and logical core count (from /proc/cpuinfo)."""
+    name, n = None, 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name") and name is None:
+                    name = line.split(":", 1)[1].strip()
+                if line.startswith("processor"):
+                    n += 1
+    except OSError:
+        pass
+    return dict(model=name, logical_cpus=n or None, usable_cpus=len(os.sched_getaffinity(0)))
+
+
+def gpu_state():
+    """Engine clock and power of GPU 0 as amd-smi reports them after the timed
+    runs (None where the tool is missing or fails)."""
+    import subprocess
+    out = {}
+    for key, cmd in (("clock", ["amd-smi", "metric", "-g", "0", "--clock", "--json"]),
+                     ("power", ["amd-smi", "metric", "-g", "0", "--power", "--json"])):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+            out[key] = json.loads(r.stdout) if r.returncode == 0 else None
+        except (OSError, ValueError, subprocess.TimeoutExpired):
+            out[key] = None
+    return out
+
+
+def accuracy(w, q, k, v, out, heads, ora_rows):
+    """Error of the INT4 output on sampled rows (first block, a middle block,
+    the ragged tail; the given heads) against the oracle's binary64 float path
+    and against textbook fp64 attention softmax(RoPE(q) RoPE(k)^T / sqrt(D)) v
+    of the unrounded inputs."""
+    import numpy as np
+    import oracle
+    from oracle import ref_fp64
+    N = w.tokens
+    mid = N // 2 // 64 * 64
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(mid, mid + 64),
+                                     np.arange((N - 1) // 64 * 64, N)])).astype(np.int32)
+    got, ora, ref = [], [], []
+    for h in heads:
+        sl = slice(h, h + 1)
+        qh, kh, vh = (np.ascontiguousarray(x[:, :, sl]) for x in (q, k, v))
+        pro = oracle.prologue(qh, kh, vh, w.grid, w.seg, w.theta, w.rot_id)
+        ora.append(oracle.attention_rows(pro, 0, 0, rows))
+        qr = ref_fp64.rope3d(oracle.as_f32(qh), w.grid, w.seg, w.theta)[0, :, 0]
+        kr = ref_fp64.rope3d(oracle.as_f32(kh), w.grid, w.seg, w.theta)[0, :, 0]
+        ref.append(ref_fp64.attention_rows(qr, kr, oracle.as_f32(vh)[0, :, 0].astype(np.float64), rows))
+        got.append(out[0, rows, h, :].astype(np.float64))
+    got, ora, ref = np.stack(got), np.stack(ora), np.stack(ref)
+    d = got - ref
+    return dict(
+        rows=int(rows.size), heads=list(heads),
+        max_abs_vs_oracle=float(np.abs(got - ora).max()),
+        err_vs_fp64=dict(max_abs=float(np.abs(d).max()),
+                         rel_l2=float(np.linalg.norm(d) / np.linalg.norm(ref)),
+                         cosine=float((got * ref).sum() / np.sqrt((got * got).sum() * (ref * ref).sum()))),
+        note="sampled rows: first 64-row block, a middle block and the ragged tail, of the listed heads; "
+             "fp64 reference = textbook attention of the unrounded bf16 inputs with 3D RoPE, no rotation "
+             "or quantization (the method's own error)")
+
+
+def tiny_oracle_1thread():
+    """The oracle on the tiny workload (2 x 4 x 4 grid, 2 heads, D64), one
+    thread: prologue + all rows, as effective TOPS."""
+    import oracle
+    from bit_quantized_attention_rope3d_amd import inputs
+    w = inputs.get("tiny")
+    q, k, v, _ = inputs.generate(w)
+    n0 = oracle.get_threads()
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 0.5:
+            pro = oracle.prologue(q, k, v, w.grid, w.seg, w.theta, w.rot_id)
+            oracle.attention_full(pro)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+    finally:
+        oracle.set_threads(n0)
+    return dict(value=w.ops() / dt / 1e12, unit="TOPS", cores=1, seconds_per_call=dt,
+                sample="tiny workload (B1 H2 D64, 32 tokens), prologue + every row, %d calls" % reps)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -335,10 +425,16 @@ def main():
         "cpu_baseline": None,
     }
 
+    result["gpu_state_after"] = gpu_state()
+    result["host"] = cpu_model()
+    o = out4.cpu().numpy()
+    if not args.no_accuracy:
+        log("accuracy on sampled rows (oracle + fp64 reference)")
+        result["accuracy"] = accuracy(w, q, k, v, o, (0, w.heads - 1), None)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
-        o = out4.cpu().numpy()
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, o, args.cpu_seconds)
+        result["cpu_baseline"]["tiny_1thread"] = tiny_oracle_1thread()
     print(json.dumps(result), flush=True)
 
 
