@@ -217,8 +217,12 @@ def cpu_model():
 
 def gpu_state():
     """Engine clock and power of GPU 0 as amd-smi reports them after the timed
-    runs (None where the tool is missing or fails)."""
+    runs (None where the tool is missing or fails, and not read under a
+    profiler, whose preloaded library would initialise the GPU in the child
+    process before it starts amd-smi)."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     out = {}
     for key, cmd in (("clock", ["amd-smi", "metric", "-g", "0", "--clock", "--json"]),
                      ("power", ["amd-smi", "metric", "-g", "0", "--power", "--json"])):
