@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -33,7 +34,7 @@ MIXED_PEAK_TFLOPS = 2.0 / (1.0 / FP6_PEAK_TFLOPS + 1.0 / FP8_PEAK_TFLOPS)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_attention_rope3d_amd", "csrc", f)
-                  for f in ("ra_int4_attn.hip", "ra_common.h")]
+                  for f in ("ra_int4_attn.hip", "ra_common.h", "ra_kernels.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_int4_flash_fwd_wan720.json")
 
 
@@ -93,13 +94,22 @@ def copy_calibration(mib):
                       "gbs_read_plus_write": gbs}), flush=True)
 
 
+def code_text(src):
+    """C++ source without comments and with runs of white space collapsed, so
+    that editing a comment does not count as changing the kernel."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_hash():
-    """Hash of the attention kernel's sources: a stored traffic figure is only
-    used while the kernel it was measured on is unchanged."""
+    """Hash of the attention kernel's code (comments and layout ignored): a
+    stored traffic figure is only used while the kernel it was measured on is
+    unchanged."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

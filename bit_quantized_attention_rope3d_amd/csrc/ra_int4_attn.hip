@@ -63,7 +63,7 @@ struct Cfg {
 template <int D>
 struct State {
   v16f acc[Cfg<D>::DT];     // O^T: sum of u * vhat, scaled by beta when m rises
-  float m;                  // running max (grid units), this lane's query
+  float m;                  // running max (log2 units), this lane's query
   v4f lsum;                 // row sum of u (16x16 MFMA accumulator; every register = this query's)
 };
 

@@ -8,8 +8,8 @@
  * pith.science review of arXiv 2607.02584):
  *   1. 3D RoPE over frame / height / width head-dim segments (Sec. 3, Fig. 2);
  *   2. a RoPE-aware 2x2 orthogonal rotation of Q and K: Interleaved (merged
- *      into the RoPE angles) or Half (pairs each dim with its counterpart in
- *      the other half of its segment, H2 blocks) (Sec. 4.1, Fig. 3);
+ *      into the RoPE angles) or Half (dim i with dim i + L/2 inside each
+ *      segment of length L, H2 blocks) (Sec. 4.1, Fig. 3);
  *   3. symmetric INT4 Q and K per (batch, head, 64-token block), symmetric
  *      INT4 V per (batch, head, channel) (abstract);
  *   4. online-softmax attention over 64-key steps, with the normalised P

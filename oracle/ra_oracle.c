@@ -47,7 +47,7 @@ int ora_get_threads(void) { return omp_get_max_threads(); }
  * width segments, each rotated by its own axis coordinate).
  * Reading: adjacent pairs (2j, 2j+1) inside a segment of even length L;
  * frequency theta^(-2j/L); positions start at 0.  With the Interleaved
- * rotation merged ([RA] Sec. 4.1: "mergeable into RoPE"), each pair angle
+ * rotation folded into the RoPE angles ([RA] Sec. 4.1), each pair angle
  * gains +pi/4, i.e. the 2x2 block R(pi/4) is composed with R(pos*freq).
  * Angles in binary64, cos/sin rounded once to binary32.                     */
 static void seg_table(int npos, int L, double theta, int interleaved,
@@ -101,8 +101,8 @@ static void fwht_f32(float *v, int D)
 /* RoPE + RoPE-aware rotation of one token row x[D] -> y[D] (binary32).
  * Pair rotation (a, b) -> (a c - b s, a s + b c), each product rounded, then
  * the sum/difference rounded.
- * Half rotation ([RA] Sec. 4.1 / Fig. 3: each dim paired with its counterpart
- * in the other half of the segment; block H2 = (1/sqrt2)[[1,1],[1,-1]] by the
+ * Half rotation ([RA] Sec. 4.1 / Fig. 3: dim i of a segment of length L
+ * meets dim i + L/2 of the same segment; block H2 = (1/sqrt2)[[1,1],[1,-1]] by the
  * free-parameter ledger) is applied after RoPE:
  *   u' = (u + w) r,  w' = (u - w) r,  r = binary32(1/sqrt2).
  * Full rotation (the dense comparator of [RA] Figs. 4-6, which rotates all D

@@ -2,8 +2,8 @@
 
 Page: RotateAttention review -- Sec. 3 / Fig. 2 (head dims split into frame,
 height and width segments, each rotated by its own axis), Sec. 4.1 / Fig. 3
-(Interleaved rotation on adjacent dims, mergeable into RoPE; Half rotation
-pairing each dim with its counterpart in the other half-segment; orthogonal
+(Interleaved rotation on adjacent dims, which folds into the RoPE angles;
+Half rotation of dim i with dim i + L/2 inside a segment of length L; orthogonal
 blocks keep (QR)(KR)^T = QK^T; the SVD argument for why only orthogonal R
 keeps Q and K ranges balanced).
 """
