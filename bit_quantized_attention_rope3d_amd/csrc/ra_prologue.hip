@@ -415,11 +415,19 @@ __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 fallback preparation: RoPE in fp32 (no rotation, no quantization),
-// rounded to bf16, rows [b*h][Npad][D]; padded rows are zero.
+// rounded to bf16; padded rows are zero.  Q as rows [b*h][Npad][D]; K in
+// 64-key tiles of 16-byte chunks, chunk (c / 8, key) of a tile at byte
+// (c / 8 * 64 + key) * 16 (channels 8 (c / 8) .. + 7 of that key), the order
+// in which the attention kernel copies a tile into LDS and reads its MFMA
+// operands.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void k_rope_bf16(QKPrologueArgs a) {
   using PL = PairLane<D>;
   constexpr int ITERS = 16 / PL::RPI;
+  // K tile staged in LDS in its chunk order, each 64-chunk group padded by 16
+  // bytes so that the 4-byte pair writes of a row spread over the banks.
+  constexpr int GSTRIDE = 64 * 16 + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t kt[(D / 8) * GSTRIDE];
   const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
   const int b = bh / a.H, h = bh % a.H;
   const void* x = which ? a.k : a.q;
@@ -440,17 +448,31 @@ __global__ __launch_bounds__(256) void k_rope_bf16(QKPrologueArgs a) {
       if (ok) load_pair<BF16>(x, (row0 + (size_t)it * PL::RPI * a.H) * D + 2 * pl.j, x0, x1);
       float v0, v1;
       pl.rope(ok ? gp.axis(pl.s) : 0, x0, x1, v0, v1);
-      *reinterpret_cast<uint32_t*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + 2 * pl.j) =
-          (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+      const uint32_t w = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+      if (which)
+        *reinterpret_cast<uint32_t*>(kt + (2 * pl.j / 8) * GSTRIDE + r * 16 + (2 * pl.j % 8) * 2) = w;
+      else
+        *reinterpret_cast<uint32_t*>(out + ((size_t)bh * a.Npad + blk * kBlock + r) * D + 2 * pl.j) = w;
       gp.advance(PL::RPI, a.tabs);
     }
   };
   if ((blk + 1) * kBlock <= a.N) rows(std::false_type{});
   else rows(std::true_type{});
+  if (which) {
+    __syncthreads();
+    // 16-byte unit u of the tile = chunk (u / 64, u % 64), at byte 16 u.
+    uint8_t* tile = reinterpret_cast<uint8_t*>(out + ((size_t)bh * a.Npad + (size_t)blk * kBlock) * D);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      *reinterpret_cast<uint4*>(tile + 16 * u) = *reinterpret_cast<const uint4*>(kt + (u >> 6) * GSTRIDE + (u & 63) * 16);
+    }
+  }
 }
 
-// V for the bf16 path: per 64-key block, [d][64 slots] bf16 in the bf16 PV
-// operand slot order; padded keys are zero.
+// V for the bf16 path: per 64-key block, 16-byte chunks (slot group g,
+// channel d) at byte (g D + d) * 16, each the 8 keys of slots 8g .. 8g + 7 in
+// the bf16 PV operand slot order; padded keys are zero.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void k_v_bf16(VQuantArgs a) {
   constexpr int PER = D / 4;
@@ -482,7 +504,7 @@ __global__ __launch_bounds__(256) void k_v_bf16(VQuantArgs a) {
       float x1 = tile[slot_key_bf16(g * 8 + 2 * e + 1)][d];
       w[e] = (uint32_t)f32_to_bf16_bits(x0) | ((uint32_t)f32_to_bf16_bits(x1) << 16);
     }
-    uint4* dst = reinterpret_cast<uint4*>(outp + (((size_t)bh * a.nkb + kb) * D + d) * 64 + g * 8);
+    uint4* dst = reinterpret_cast<uint4*>(outp + ((size_t)bh * a.nkb + kb) * D * 64 + (g * D + d) * 8);
     *dst = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
