@@ -217,9 +217,11 @@ __device__ __forceinline__ void fwht_row(float (&x)[VEC]) {
 // 3 (Full) multiplies the whole RoPE'd row by the Walsh-Hadamard matrix.  The
 // rotated values stay in registers for the block amax, then become fp6 e2m3
 // codes, one per byte in an LDS tile, which the workgroup packs into the
-// 64-token fp6 tile and writes with coalesced 16-byte stores.
+// 64-token fp6 tile and writes with coalesced 16-byte stores.  Eight waves
+// per SIMD (64 registers, a few spilled): the loads of more blocks in flight
+// outweigh the spills in this latency-bound pass.
 template <int ROT, bool BF16, int D>
-__global__ __launch_bounds__(256) void k_rope_quant_qk(QKPrologueArgs a) {
+__global__ __launch_bounds__(256, 8) void k_rope_quant_qk(QKPrologueArgs a) {
   using PL = PairLane<D>;
   constexpr int ITERS = 16 / PL::RPI;
   __shared__ float red[4];
@@ -372,22 +374,41 @@ __global__ void k_zero_u32(uint32_t* p, size_t n) {
 template <bool BF16, int D, bool VH>
 __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
   constexpr int PER = D / 4;
-  __shared__ float tile[64][D + 1];
+  // bf16 inputs without the Hadamard are held in LDS as their bf16 bits
+  // (exact, and half the LDS, so more workgroups fit on a CU); otherwise fp32.
+  constexpr bool RAW = BF16 && !VH;
+  typedef typename std::conditional<RAW, uint16_t, float>::type TT;
+  __shared__ TT tile[64][D + 2];
   const int kb = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
   const int t = threadIdx.x, r = t >> 2, qq = t & 3;
   const int n = kb * kBlock + r;
-  float tmp[PER];
-  if (n < a.N) {
-    load_row_part<BF16>(a.v, (((size_t)b * a.N + n) * a.H + h) * D + qq * PER, PER, tmp);
+  if constexpr (RAW) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) +
+                                                      (((size_t)b * a.N + (n < a.N ? n : 0)) * a.H + h) * D + qq * PER);
+#pragma unroll
+    for (int i = 0; i < PER / 8; ++i) {
+      const uint4 w = n < a.N ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[r][qq * PER + 8 * i]);
+      dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
+    }
   } else {
+    float tmp[PER];
+    if (n < a.N) {
+      load_row_part<BF16>(a.v, (((size_t)b * a.N + n) * a.H + h) * D + qq * PER, PER, tmp);
+    } else {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) tmp[e] = 0.0f;
+      for (int e = 0; e < PER; ++e) tmp[e] = 0.0f;
+    }
+    if (VH) fwht_row<PER, D>(tmp);       // lanes 4r .. 4r+3 hold row r (padded rows stay 0)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = tmp[e];
   }
-  if (VH) fwht_row<PER, D>(tmp);       // lanes 4r .. 4r+3 hold row r (padded rows stay 0)
-#pragma unroll
-  for (int e = 0; e < PER; ++e) tile[r][qq * PER + e] = tmp[e];
   __syncthreads();
+  auto val = [&](int key, int d) -> float {
+    if constexpr (RAW) return __uint_as_float((uint32_t)tile[key][d] << 16);
+    else return tile[key][d];
+  };
 
   if (t < 2 * D) {
     const int d = t >> 1, hf = t & 1;
@@ -400,7 +421,7 @@ __global__ __launch_bounds__(256) void k_v_quant(VQuantArgs a) {
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         const int key = slot_key_pv(v6_slot(hf, 4 * q4 + bi));
-        const int c = amax > 0.0f ? quant_code(tile[key][d], inv) : 0;
+        const int c = amax > 0.0f ? quant_code(val(key, d), inv) : 0;
         acc |= e2m3_of_code(c) << (8 * bi);
       }
       cw[q4] = acc;
