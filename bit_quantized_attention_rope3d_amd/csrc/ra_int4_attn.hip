@@ -759,34 +759,49 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
       }
     fwht_out<D>(st.acc);
   }
-  const int q = q0 + ln;
-  if (q < a.N) {
-    const int b = bh / a.H, h = bh % a.H;
-    const size_t obase = (((size_t)b * a.N + q) * a.H + h) * D;
+  // The rows leave through LDS, one 32-channel tile at a time: each lane
+  // holds 4-channel pieces of one query, so direct stores would write every
+  // row in 32-byte pieces; staged, a store instruction writes whole 128-byte
+  // row segments.  Each wave stages its 32 rows in its own LDS region (the
+  // K/V stages, free once every wave has left the key loop).
+  __syncthreads();
+  constexpr uint32_t kRowB = 32 * 4 + 16;                   // staged row: 32 fp32 channels, padded
+  const uint32_t obuf = (uint32_t)wave * 32u * kRowB;
+  const int b = bh / a.H, h = bh % a.H;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+  for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = dt * 32 + 8 * g + 4 * hf;
-        float o[4];
-        if (VH) {
+    for (int g = 0; g < 4; ++g) {
+      const int d = dt * 32 + 8 * g + 4 * hf;
+      v4f o;
+      if (VH) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = st.acc[dt][4 * g + e];
-        } else {
-          const v4f sv = *reinterpret_cast<const v4f*>(a.s_v + (size_t)bh * D + d);
+        for (int e = 0; e < 4; ++e) o[e] = st.acc[dt][4 * g + e];
+      } else {
+        const v4f sv = *reinterpret_cast<const v4f*>(a.s_v + (size_t)bh * D + d);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = st.acc[dt][4 * g + e] * sv[e] * inv;
-        }
+        for (int e = 0; e < 4; ++e) o[e] = st.acc[dt][4 * g + e] * sv[e] * inv;
+      }
+      *reinterpret_cast<__attribute__((address_space(3))) v4f*>(obuf + ln * kRowB + (8 * g + 4 * hf) * 4) = o;
+    }
+    // Read back by the same wave (its LDS accesses stay in order): lane l
+    // takes 16 bytes of row 8 i + l / 8.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + (lane >> 3), c = lane & 7;
+      const v4f o = *reinterpret_cast<const __attribute__((address_space(3))) v4f*>(obuf + r * kRowB + c * 16);
+      const int q = q0 + r;
+      if (q < a.N) {
+        const size_t oe = (((size_t)b * a.N + q) * a.H + h) * D + dt * 32 + 4 * c;
         if (OUT_BF16) {
-          uint16_t* op = static_cast<uint16_t*>(a.out) + obase + d;
-          *reinterpret_cast<uint2*>(op) =
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oe) =
               make_uint2((uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16),
                          (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16));
         } else {
-          float* op = static_cast<float*>(a.out) + obase + d;
-          *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oe) = make_float4(o[0], o[1], o[2], o[3]);
         }
       }
+    }
   }
 }
 
