@@ -125,18 +125,6 @@ __device__ __forceinline__ void load_pair(const void* base, size_t elem_off, flo
   }
 }
 
-// fp6 e2m3 bits of the INT4 code of x: q = clamp(rint(x inv), -7, 7) as a
-// float (+0.0 turns -0 into +0), then the e2m3 fields read off its fp32
-// bits: for |q| in [1, 8) the exponent field is E + 1 and the mantissa the
-// top three fp32 mantissa bits, i.e. (bits >> 20) - 0x3F0 on the magnitude;
-// q = 0 saturates to 0.
-__device__ __forceinline__ uint32_t quant_e2m3(float x, float inv) {
-  const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(x * inv), -7.0f, 7.0f) + 0.0f;
-  const uint32_t b = __float_as_uint(q);
-  const uint32_t mag = __builtin_elementwise_sub_sat((b >> 20) & 0x7FFu, 0x3F0u);
-  return mag | ((b >> 26) & 0x20u);
-}
-
 __device__ __forceinline__ int quant_code(float x, float inv) {
   float q = __builtin_rintf(x * inv);
   q = fminf(fmaxf(q, -7.0f), 7.0f);
@@ -215,9 +203,10 @@ __device__ __forceinline__ void fwht_row(float (&x)[VEC]) {
 // (i, i + L/2) of each segment through a per-wave LDS row, r = f32(1/sqrt 2);
 // ROT == 1 (Interleaved) is already merged into the tables as +pi/4; ROT ==
 // 3 (Full) multiplies the whole RoPE'd row by the Walsh-Hadamard matrix.  The
-// rotated values stay in registers for the block amax, then become fp6 e2m3
-// codes, one per byte in an LDS tile, which the workgroup packs into the
-// 64-token fp6 tile and writes with coalesced 16-byte stores.  Eight waves
+// rotated values stay in registers for the block amax, then become INT4
+// codes held as fp16 values in an LDS tile; one conversion instruction per
+// (token, 32-channel group) packs them into the fp6 e2m3 string of the
+// 64-token tile, written with coalesced stores.  Eight waves
 // per SIMD (64 registers, a few spilled): the loads of more blocks in flight
 // outweigh the spills in this latency-bound pass.
 template <int ROT, bool BF16, int D>
@@ -225,7 +214,11 @@ __global__ __launch_bounds__(256, 8) void k_rope_quant_qk(QKPrologueArgs a) {
   using PL = PairLane<D>;
   constexpr int ITERS = 16 / PL::RPI;
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t cb[kBlock * D];   // e2m3 code per byte, [row][channel]
+  // The block's codes as fp16 values (exact for -7..7), [row][channel],
+  // rows padded by 16 bytes so that the 64-byte group reads spread over the
+  // banks.
+  constexpr int kCbRow = 2 * D + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t cb[kBlock * kCbRow];
   const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
   const int b = bh / a.H, h = bh % a.H;
   const void* x = which ? a.k : a.q;
@@ -300,31 +293,33 @@ __global__ __launch_bounds__(256, 8) void k_rope_quant_qk(QKPrologueArgs a) {
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int r = r0 + it * PL::RPI;
-    const uint32_t c0 = amax > 0.0f ? quant_e2m3(y[it][0], inv) : 0u;
-    const uint32_t c1 = amax > 0.0f ? quant_e2m3(y[it][1], inv) : 0u;
-    *reinterpret_cast<uint16_t*>(cb + r * D + 2 * pl.j) = (uint16_t)(c0 | (c1 << 8));
+    // q = clamp(rint(x inv), -7, 7) (+ 0.0 turns -0 into +0); both codes of
+    // the pair as fp16 (exact) in one 4-byte LDS word.
+    const float q0 = amax > 0.0f ? __builtin_amdgcn_fmed3f(__builtin_rintf(y[it][0] * inv), -7.0f, 7.0f) + 0.0f : 0.0f;
+    const float q1 = amax > 0.0f ? __builtin_amdgcn_fmed3f(__builtin_rintf(y[it][1] * inv), -7.0f, 7.0f) + 0.0f : 0.0f;
+    *reinterpret_cast<uint32_t*>(cb + r * kCbRow + 4 * pl.j) =
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(q0, q1));
   }
   if (threadIdx.x == 0) sc[(size_t)bh * a.nblk + blk] = amax > 0.0f ? scale : 0.0f;
   __syncthreads();
 
-  // The tile in 16-byte units: unit u < 2D is bits 0..127 of (row u % 64,
-  // group u / 64); unit 2D + v is bits 128..191 of rows 2(v % 32) and
-  // 2(v % 32) + 1 of group v / 32.  Unit u lands at byte 16 u of the tile.
+  // One (row r, channel group g) per thread: its 32 codes become the 192-bit
+  // fp6 e2m3 string (code i at bits 6i .. 6i+5) in one conversion
+  // instruction; bits 0..127 go to byte (64 g + r) 16 of the tile, bits
+  // 128..191 to byte (D / 32) 1024 + (64 g + r) 8.
   uint8_t* tile = out + ((size_t)bh * a.Npad + (size_t)blk * kBlock) * (qk6_tile_bytes(D) / kBlock);
-  for (int u = threadIdx.x; u < 3 * D; u += 256) {
-    uint4 o;
-    if (u < 2 * D) {
-      uint32_t cw[8];
-      load_group_codes(cb + (u & 63) * D + 32 * (u >> 6), cw);
-      o = make_uint4(fp6_word<0>(cw), fp6_word<1>(cw), fp6_word<2>(cw), fp6_word<3>(cw));
-    } else {
-      const int v = u - 2 * D, g = v >> 5, r = 2 * (v & 31);
-      uint32_t c0w[8], c1w[8];
-      load_group_codes(cb + r * D + 32 * g, c0w);
-      load_group_codes(cb + (r + 1) * D + 32 * g, c1w);
-      o = make_uint4(fp6_word<4>(c0w), fp6_word<5>(c0w), fp6_word<4>(c1w), fp6_word<5>(c1w));
-    }
-    *reinterpret_cast<uint4*>(tile + 16 * u) = o;
+  for (int u = threadIdx.x; u < 2 * D; u += 256) {
+    const int r = u & 63, g = u >> 6;
+    typedef __fp16 v32h __attribute__((ext_vector_type(32)));
+    typedef uint32_t v6u __attribute__((ext_vector_type(6)));
+    const uint4* src = reinterpret_cast<const uint4*>(cb + r * kCbRow + 64 * g);
+    const uint4 c0 = src[0], c1 = src[1], c2 = src[2], c3 = src[3];
+    const uint32_t cw[16] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
+                             c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
+    const v32h codes = __builtin_bit_cast(v32h, cw);
+    const v6u w = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(codes, 1.0f);
+    *reinterpret_cast<uint4*>(tile + (64 * g + r) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint2*>(tile + (D / 32) * 1024 + (64 * g + r) * 8) = make_uint2(w[4], w[5]);
   }
 }
 
