@@ -654,17 +654,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   state_init<D>(st);
   uint32_t dsum = 0, dhash = 0;                             // DUMP only
 
-  // Step t: P codes of step t (S in registers), S of step t+1, P x V of step
-  // t, then the running max of step t+1 and the rescale it may need.  Within
-  // a wave these run in order; the other two waves on the SIMD fill the
-  // latencies.  K/V tiles live in kStages = 2 kSync LDS stages and the
-  // workgroup barrier is taken once every kSync steps, so the waves of a
-  // SIMD drift apart within a block of steps instead of meeting in the same
-  // phase every step.  At step t each wave issues its share of the copies
-  // of K of step t + kSync + 1 (S of a step is made one step ahead) and V
-  // of step t + kSync.  A stage is rewritten only after the barrier that
-  // ends the last step reading it, and a tile is read only after the
-  // barrier that follows its copy.
+  // Step t: P x V of step t - 1 (its MFMAs are issued first and run while
+  // the codes of step t are made from S in registers), the rescale the
+  // accumulators need before P x V of step t, then S and the running max of
+  // step t+1.  The other two waves on the SIMD fill the latencies.  K/V
+  // tiles live in kStages = 2 kSync LDS stages and the workgroup barrier is
+  // taken once every kSync steps (after the steps t with t % kSync == 0), so
+  // the waves of a SIMD drift apart within a block of steps instead of
+  // meeting in the same phase every step.  At step t each wave issues its
+  // share of the copies of K of step t + kSync + 1 (read by step t + kSync
+  // for S of step t + kSync + 1) and V of step t + kSync - 1 (read by step
+  // t + kSync for P x V of step t + kSync - 1): every tile is read kSync
+  // steps after its copy, so a barrier always lies between the two, and the
+  // stage a copy overwrites was last read kSync steps before it.
   const TileDma<D, kWaves> dma;
   const uint8_t* const ktiles = a.kp + (size_t)bh * a.nblk * C::KT;
   const uint8_t* const vtiles = a.vp + (size_t)bh * a.nkb * C::VT;
@@ -678,7 +680,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   __syncthreads();
 #pragma unroll
   for (int i = 1; i <= kSync; ++i)
-    dma.issue(i < nkb ? ktiles + i * C::KT : nullptr, i - 1 < nkb ? vtiles + (i - 1) * C::VT : nullptr,
+    dma.issue(i < nkb ? ktiles + i * C::KT : nullptr, i < kSync && i - 1 < nkb ? vtiles + (i - 1) * C::VT : nullptr,
               kst(i), vst(i - 1));
   v16f s[2];
   qk_step<D>(kst(0), qop, s);
@@ -696,26 +698,45 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     else return sk;
   }();
   const uint8_t* ktn = ktiles + (kSync + 1) * C::KT;   // K tile of step t + kSync + 1
-  const uint8_t* vtn = vtiles + kSync * C::VT;         // V tile of step t + kSync
-  // One step; RAGGED: step t+1 may be the last one, with N ending inside it.
-  auto step = [&](int t, auto ragged, auto sync) {
-    dma.issue(t + kSync + 1 < nkb ? ktn : nullptr, t + kSync < nkb ? vtn : nullptr, kst(t + kSync + 1),
-              vst(t + kSync));
+  const uint8_t* vtn = vtiles + (kSync - 1) * C::VT;   // V tile of step t + kSync - 1
+  float m_prev = -INFINITY;                             // running max before step t
+  uint32_t pp[2][4];                                    // codes of step t - 1
+  // One step t < nkb - 1: P x V of step t - 1 (its MFMAs run under this
+  // step's P-map work), the codes of step t, the rescale by
+  // 2^(m(t-1) - m(t)) the accumulators need before P x V of step t, then S
+  // and the running max of step t+1.  FIRST: t = 0; RAGGED: step t+1 may be
+  // the last one.
+  auto step = [&](int t, auto ragged, auto sync, auto first) {
+    dma.issue(t + kSync + 1 < nkb ? ktn : nullptr, t + kSync - 1 < nkb ? vtn : nullptr, kst(t + kSync + 1),
+              vst(t + kSync - 1));
+    if constexpr (!decltype(first)::value) {
+      pv_step<D>(vst(t - 1), pp, st.acc);
+      lsum_step(lsum_selector_at_use(), pp, st.lsum);
+    }
     uint32_t p[2][4];
     pmap_codes(s, cp_cur * kPIdxScale, st.m * kPIdxScale + 0.0f, a.pm.top_sub, ptab, p);
     if constexpr (DUMP) row_digest(p, t, dsum, dhash);
+    if constexpr (!decltype(first)::value) {
+      if (__ballot(st.m > m_prev) != 0) {
+        const float beta = exp2f(m_prev - st.m);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st.acc[dt][r] *= beta;
+        st.lsum *= beta;
+      }
+    }
     qk_step<D>(kst(t + 1), qop, s);       // S of step t+1
-    pv_step<D>(vst(t), p, st.acc);
-    lsum_step(lsum_selector_at_use(), p, st.lsum);
     if constexpr (decltype(ragged)::value) {
       const int nv1 = a.N - (t + 1) * kBlock;
       if (nv1 < kBlock) mask_scores(s, opaque_sgpr(nv1));
     }
     const float cp_next = score_scale(cq, skp[t + 1], a.alpha);
-    const float m_new = running_max(s, cp_next, st.m);
-    if (__ballot(m_new > st.m) != 0) rescale<D>(st, m_new);
-    st.m = m_new;
+    m_prev = st.m;
+    st.m = running_max(s, cp_next, st.m);
     cp_cur = cp_next;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pp[i >> 2][i & 3] = p[i >> 2][i & 3];
     if constexpr (decltype(sync)::value) {
       wait_lds_dma();
       __syncthreads();
@@ -723,28 +744,53 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
     ktn += C::KT;
     vtn += C::VT;
   };
-  int t0 = 0;
-  // Whole blocks in which no step is followed by the last one.
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (nkb > 1) {
+    // Barriers after the steps t with t % kSync == 0.
+    step(0, T_{}, T_{}, T_{});
+    int t0 = 1;
+    // Whole blocks in which no step is followed by the last one.
 #pragma nounroll
-  for (; t0 + kSync + 1 < nkb; t0 += kSync) {
+    for (; t0 + kSync + 1 < nkb; t0 += kSync) {
 #pragma unroll
-    for (int i = 0; i + 1 < kSync; ++i) step(t0 + i, std::false_type{}, std::false_type{});
-    step(t0 + kSync - 1, std::false_type{}, std::true_type{});
-  }
-  // The remaining steps but the last, with a barrier after each.
+      for (int i = 0; i + 1 < kSync; ++i) step(t0 + i, F_{}, F_{}, F_{});
+      step(t0 + kSync - 1, F_{}, T_{}, F_{});
+    }
+    // The remaining steps but the last, with a barrier after each.
 #pragma nounroll
-  for (; t0 + 1 < nkb; ++t0) step(t0, std::true_type{}, std::true_type{});
-  {
-    // The last step: its V tile is resident since the barrier before it.
+    for (; t0 + 1 < nkb; ++t0) step(t0, T_{}, T_{}, F_{});
+    // The last step: P x V of step t - 1, the rescale, its codes, and its
+    // own P x V after a barrier (its V tile was copied fewer than kSync
+    // steps ago).
     const int t = nkb - 1, nvalid = a.N - t * kBlock;
+    pv_step<D>(vst(t - 1), pp, st.acc);
+    lsum_step(lsum_selector_at_use(), pp, st.lsum);
     uint32_t p[2][4];
     pmap_codes(s, cp_cur * kPIdxScale, st.m * kPIdxScale + 0.0f, a.pm.top_sub, ptab, p);
     if (nvalid < kBlock) mask_p(p, nvalid);
     if constexpr (DUMP) row_digest(p, t, dsum, dhash);
+    if (__ballot(st.m > m_prev) != 0) {
+      const float beta = exp2f(m_prev - st.m);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.acc[dt][r] *= beta;
+      st.lsum *= beta;
+    }
+    wait_lds_dma();
+    __syncthreads();
     pv_step<D>(vst(t), p, st.acc);
     lsum_step(lsum_selector_at_use(), p, st.lsum);
+  } else {
+    // A single key step (N <= 64).
+    uint32_t p[2][4];
+    pmap_codes(s, cp_cur * kPIdxScale, st.m * kPIdxScale + 0.0f, a.pm.top_sub, ptab, p);
+    if (a.N < kBlock) mask_p(p, a.N);
+    if constexpr (DUMP) row_digest(p, 0, dsum, dhash);
+    pv_step<D>(vst(0), p, st.acc);
+    lsum_step(lsum_selector_at_use(), p, st.lsum);
   }
-
 
   if constexpr (DUMP) {
     dsum = xhalf_sum_u(dsum);
