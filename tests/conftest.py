@@ -10,6 +10,8 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    import progress
+    progress.CAPMAN = config.pluginmanager.getplugin("capturemanager")
 
 
 @pytest.fixture(scope="session")

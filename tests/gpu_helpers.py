@@ -1,10 +1,10 @@
 """Shared helpers of the GPU parity tests (host-side marshalling only)."""
 from __future__ import annotations
 
-import sys
-
 import numpy as np
 import torch
+
+import progress
 
 # INT4 output against the oracle's binary64 float path: max-abs bound.  The
 # integers (codes, scores, P codes, PV sums, running max) are exact on both
@@ -15,8 +15,7 @@ OUT_TOL = 1e-5
 
 
 def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
+    progress.say(*a)
 
 
 def dev(x: np.ndarray) -> torch.Tensor:
