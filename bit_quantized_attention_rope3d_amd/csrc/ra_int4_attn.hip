@@ -444,14 +444,19 @@ __device__ __forceinline__ void pv_step(uint32_t vst, const uint32_t (&p)[2][4],
                      (int)p[1][0], (int)p[1][1], (int)p[1][2], (int)p[1][3]};
   lds_cu8* const vlo = lds_base(vst + v6_lo_off(D, ln, hf));
   lds_cu8* const vhi = lds_base(vst + v6_hi_off(D, ln, hf));
+  // All V operands are read before the first MFMA, so that the LDS latency
+  // is paid once per step rather than once per MFMA.
+  v8i va[Cfg<D>::DT];
 #pragma unroll
   for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
     const v4i lo = lds_ld<v4i>(vlo + 512 * dt);
     const v2i hi = lds_ld<v2i>(vhi + 256 * dt);
     operand_fence();
-    const v8i va = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
-    acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[dt], 2, 0, 0, 0, 0, 0);
+    va[dt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
   }
+#pragma unroll
+  for (int dt = 0; dt < Cfg<D>::DT; ++dt)
+    acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[dt], pb, acc[dt], 2, 0, 0, 0, 0, 0);
 }
 
 // The running max rises from st.m to m_new: A = A * beta, L = (L + U) * beta.
