@@ -96,6 +96,43 @@ ra::PMapArgs pmap_args(int p_mode) {
   return pm;
 }
 
+// e4m3 byte of an integer 0 <= u <= 15 (exact): the PV operand format of u.
+uint8_t e4m3_of_uint(uint32_t u) {
+  if (u == 0) return 0;
+  int e = 0;
+  while ((u >> (e + 1)) != 0) ++e;                       // floor(log2 u) <= 3
+  return (uint8_t)(((e + 7) << 3) | ((u << (3 - e)) & 7u));
+}
+
+// The kernels' P-map table (layout in ra_kernels.h, kPTabTotal bytes): the
+// entry at address a is for cell j = top - a; it counts the X_k whose cell
+// lies above j, plus the X_k whose cell is j when that cell holds nothing
+// above X_k; a cell that does is marked 0x80 | k.  Addresses past top stay 0.
+std::vector<uint8_t> pmap_table(const ra::PMapArgs& pm) {
+  std::vector<uint8_t> t(ra::kPTabTotal, 0);
+  for (int a = 0; a <= pm.top; ++a) {
+    const int j = pm.top - a;
+    uint32_t u = 0, mark = 0;
+    for (int k = 0; k < pm.P; ++k) {
+      const bool split = (pm.split >> k) & 1u;
+      if (j < pm.cell[k] || (j == pm.cell[k] && !split)) ++u;
+      if (j == pm.cell[k] && split) mark = 0x80u | (uint32_t)k;
+    }
+    t[a] = (uint8_t)(mark ? mark : e4m3_of_uint(u));
+  }
+  for (int k = 0; k < 16; ++k) {
+    const float thr = k < pm.P ? pm.ythr[k] : 0.0f;
+    std::memcpy(&t[ra::kPTabBytes + 8 * k], &thr, 4);
+    t[ra::kPTabBytes + 8 * k + 4] = e4m3_of_uint((uint32_t)k);
+    t[ra::kPTabBytes + 8 * k + 5] = e4m3_of_uint((uint32_t)k + 1);
+  }
+  return t;
+}
+
+// Bytes of RoPE tables in a plan's device buffer, rounded up to 16: the
+// P-map table follows them.
+size_t ptab_offset(size_t tab_floats) { return (tab_floats * sizeof(float) + 15) & ~(size_t)15; }
+
 struct Layout {
   int N, Npad, nblk, nkb, nqt;
   size_t off_q, off_k, off_v, off_sq, off_sk, off_sv, off_vamax, off_dbg, total;
@@ -229,22 +266,41 @@ ra_status upload_tables(ra_plan p) {
   std::lock_guard<std::mutex> g(p->mu);
   if (p->dev_tabs.count(dev)) return RA_OK;
   float* buf = nullptr;
-  if (hipMalloc(&buf, p->tab_floats * sizeof(float)) != hipSuccess) {
+  const size_t bytes = ptab_offset(p->tab_floats) + ra::kPTabTotal;
+  if (hipMalloc(&buf, bytes) != hipSuccess) {
     (void)hipGetLastError();
-    return fail(RA_ERR_OOM, "hipMalloc of %zu bytes of RoPE tables failed", p->tab_floats * sizeof(float));
+    return fail(RA_ERR_OOM, "hipMalloc of %zu bytes of plan tables failed", bytes);
   }
-  std::vector<float> host;
-  host.reserve(p->tab_floats);
-  for (int s = 0; s < 3; ++s)      // (cos, sin) interleaved: one 8-byte load per pair
+  // (cos, sin) interleaved, one 8-byte load per pair, then the P-map table.
+  std::vector<uint8_t> host(bytes, 0);
+  size_t o = 0;
+  for (int s = 0; s < 3; ++s)
     for (size_t i = 0; i < p->cs[s].size(); ++i) {
-      host.push_back(p->cs[s][i]);
-      host.push_back(p->sn[s][i]);
+      std::memcpy(&host[o], &p->cs[s][i], 4);
+      std::memcpy(&host[o + 4], &p->sn[s][i], 4);
+      o += 8;
     }
-  if (hipMemcpy(buf, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+  const std::vector<uint8_t> pt = pmap_table(p->pm);
+  std::memcpy(&host[ptab_offset(p->tab_floats)], pt.data(), pt.size());
+  if (hipMemcpy(buf, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
     hipFree(buf);
-    return fail(RA_ERR_HIP, "copying RoPE tables to device %d failed", dev);
+    return fail(RA_ERR_HIP, "copying plan tables to device %d failed", dev);
   }
   p->dev_tabs[dev] = buf;
+  return RA_OK;
+}
+
+// The current device's copy of the P-map table (no allocation, no copy).
+ra_status device_ptab(ra_plan p, const uint8_t** t) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(RA_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> g(p->mu);
+  auto it = p->dev_tabs.find(dev);
+  if (it == p->dev_tabs.end())
+    return fail(RA_ERR_INVALID_ARG,
+                "the plan has no tables on device %d: create it with that device current, "
+                "or call ra_plan_upload there first", dev);
+  *t = reinterpret_cast<const uint8_t*>(it->second) + ptab_offset(p->tab_floats);
   return RA_OK;
 }
 
@@ -464,6 +520,7 @@ ra_status ra_attn_main(ra_plan p, void* o, void* ws, size_t ws_bytes, hipStream_
   if (st != RA_OK) return st;
   if (inject("launch")) return fail(RA_ERR_HIP, "injected launch failure (RA_FAULT_INJECT=launch)");
   ra::AttnArgs a = attn_args(p, static_cast<uint8_t*>(ws), o);
+  if (p->opts.prec == RA_PREC_INT4 && (st = device_ptab(p, &a.ptab)) != RA_OK) return st;
   const bool out_bf16 = p->opts.out_dtype == RA_DT_BF16;
   if (p->opts.prec == RA_PREC_INT4)
     ra::launch_int4_attn(a, p->shape.head_dim, out_bf16, p->shape.batch, stream);
@@ -646,6 +703,7 @@ ra_status ra_debug_tile(ra_plan p, void* ws, size_t ws_bytes, int32_t b, int32_t
   uint8_t* w = static_cast<uint8_t*>(ws);
   const int D = p->shape.head_dim;
   ra::AttnArgs a = attn_args(p, w, nullptr);
+  if ((st = device_ptab(p, &a.ptab)) != RA_OK) return st;
   ra::TileDumpArgs t{};
   uint8_t* dbg = w + p->lay.off_dbg;
   t.s_int = reinterpret_cast<int32_t*>(dbg);
@@ -677,6 +735,7 @@ ra_status ra_debug_row_digests(ra_plan p, void* o, void* ws, size_t ws_bytes, ui
   ra_status st = check_ws(p, ws, ws_bytes);
   if (st != RA_OK) return st;
   ra::AttnArgs a = attn_args(p, static_cast<uint8_t*>(ws), o);
+  if ((st = device_ptab(p, &a.ptab)) != RA_OK) return st;
   a.row_dbg = rows;
   ra::launch_int4_attn_rowdbg(a, p->shape.head_dim, p->shape.batch, stream);
   st = after_launch("attention (row digests)");
@@ -687,7 +746,33 @@ ra_status ra_debug_pmap(const float* d, uint8_t* u, int64_t n, int32_t p_mode, h
   if (n < 0) return fail(RA_ERR_INVALID_ARG, "n must be >= 0");
   if (n > 0 && (!d || !u)) return fail(RA_ERR_INVALID_ARG, "d and u must be non-null");
   if (p_mode != 0 && p_mode != 1) return fail(RA_ERR_INVALID_ARG, "p_mode %d is not 0 or 1", p_mode);
-  ra::launch_pmap_probe(d, u, n, pmap_args(p_mode), stream);
+  // The table the attention kernels use, built and copied to the current
+  // device once per P mode (kept until the process ends).
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, uint8_t*> tabs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(RA_ERR_HIP, "hipGetDevice failed");
+  const ra::PMapArgs pm = pmap_args(p_mode);
+  uint8_t* tab = nullptr;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = tabs.find({dev, p_mode});
+    if (it == tabs.end()) {
+      const std::vector<uint8_t> h = pmap_table(pm);
+      if (hipMalloc(&tab, h.size()) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(RA_ERR_OOM, "hipMalloc of the P-map table failed");
+      }
+      if (hipMemcpy(tab, h.data(), h.size(), hipMemcpyHostToDevice) != hipSuccess) {
+        hipFree(tab);
+        return fail(RA_ERR_HIP, "copying the P-map table failed");
+      }
+      tabs[{dev, p_mode}] = tab;
+    } else {
+      tab = it->second;
+    }
+  }
+  ra::launch_pmap_probe(d, u, n, pm, tab, stream);
   ra_status st = after_launch("pmap probe");
   return st == RA_OK ? ok() : st;
 }

@@ -98,8 +98,6 @@ struct State {
 // 0x80 | k (no e4m3 code of 0..15 has bit 7 set) and u = k + (y <= X_k / 8),
 // decided by pmap_fix after the lookup from the 8-byte record k behind the
 // table: X_k / 8, then the bytes e4m3(k) and e4m3(k + 1).
-constexpr int kPTabBytes = (kPTabEntries + 15) & ~15;       // one byte per cell, 16-byte padded
-constexpr int kPThrBytes = 16 * 8;                          // 16 records behind the table
 constexpr float kPIdxScale = 0.125f;                        // 2^-3
 constexpr uint32_t kPSplit = 0x80808080u;                   // marked entries, per packed byte
 
@@ -124,29 +122,6 @@ __device__ __forceinline__ uint32_t e4m3_to_uint(uint32_t b) {
   if (b == 0u) return 0u;
   const uint32_t e = (b >> 3) - 7u, m = b & 7u;
   return ((8u | m) << e) >> 3;
-}
-
-// Fill the table and the records behind it cooperatively (threads tid,
-// tid + nt, ...): the entry of cell j = top - a counts the X_k whose cell
-// lies above j (cell j holds only x below them), plus the X_k whose cell is
-// j when that cell holds nothing above it; a cell that does is marked with
-// its k.
-__device__ __forceinline__ void ptab_build(uint8_t* tab, int tid, int nt, const PMapArgs& pm) {
-  for (int a = tid; a <= pm.top; a += nt) {
-    const int j = pm.top - a;
-    uint32_t u = 0, mark = 0;
-    for (int k = 0; k < pm.P; ++k) {
-      const bool split = (pm.split >> k) & 1u;
-      if (j < pm.cell[k] || (j == pm.cell[k] && !split)) ++u;
-      if (j == pm.cell[k] && split) mark = 0x80u | (uint32_t)k;
-    }
-    tab[a] = (uint8_t)(mark ? mark : e4m3_of_uint(u));
-  }
-  uint32_t* rec = reinterpret_cast<uint32_t*>(tab + kPTabBytes);
-  for (int k = tid; k < 16; k += nt) {
-    rec[2 * k] = __float_as_uint(k < pm.P ? pm.ythr[k] : 0.0f);
-    rec[2 * k + 1] = e4m3_of_uint((uint32_t)k) | (e4m3_of_uint((uint32_t)k + 1u) << 8);
-  }
 }
 
 // ---- K/V staging: global memory -> LDS without registers ------------------
@@ -176,6 +151,24 @@ __device__ __forceinline__ v4i make_rsrc(const uint8_t* base, uint32_t bytes) {
 }
 
 __device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The P-map table (entries and records, kPTabTotal bytes, built by the host)
+// into the LDS array `tab` by the NW waves of the workgroup: 16 bytes per
+// lane, 64 lanes per instruction, lanes past the end masked off.  Complete
+// after wait_lds_dma() and a barrier.  The copies' LDS address is formed
+// from the array's own address, so the compiler knows the copy statement
+// may write it (an LDS array it saw no store to could otherwise be read as
+// undefined).
+template <int NW>
+__device__ __forceinline__ void ptab_copy(const uint8_t* g, uint8_t* tab) {
+  constexpr int kChunks = kPTabTotal / 16;
+  static_assert(kPTabTotal % 16 == 0, "whole 16-byte chunks");
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)tab;
+  const v4i rsrc = make_rsrc(g, kPTabTotal);
+  for (int c = wave; 64 * c < kChunks; c += NW)
+    if (64 * c + lane < kChunks) lds_copy16(rsrc, base + (uint32_t)(1024 * c), 1024 * c + 16 * lane);
+}
 
 // Copies of one step's K tile and V tile (fp6, 48 D bytes each) by NW
 // waves.  The tiles are cut into 16-byte slots numbered in LDS order; a wave
@@ -626,7 +619,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_int4_attn(AttnArgs a) {
   uint8_t* const ptab = smem;                               // P-map table at LDS address 0
   float* const skl = reinterpret_cast<float*>(smem + kPTabBytes + kPThrBytes + kStages * (C::KT + C::VT));
 
-  ptab_build(ptab, threadIdx.x, 64 * kWaves, a.pm);         // visible after the first barrier
+  ptab_copy<kWaves>(a.ptab, ptab);                          // visible after the first barrier
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of (head, query-tile) ids.
@@ -876,7 +869,7 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPTabBytes + kPThrBytes + C::KT + C::VT];
   uint8_t* const ptab = smem;
   constexpr uint32_t tiles = kPTabBytes + kPThrBytes;      // LDS address of the K tile, then the V tile
-  ptab_build(ptab, threadIdx.x, 128, a.pm);
+  ptab_copy<2>(a.ptab, ptab);                               // visible after the first barrier
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, ln = lane & 31;
   const int bh = t.bh;
   const int q0 = t.q_blk * kBlock + wave * 32;
@@ -906,9 +899,10 @@ __global__ __launch_bounds__(128) void k_int4_tile_dump(AttnArgs a, TileDumpArgs
 // m = 0 (so x = -d exactly).  Each lane maps 32 consecutive values, as a
 // lane maps its 32 scores of a step; u = code + zero-point.
 __global__ __launch_bounds__(256) void k_pmap_probe(const float* __restrict__ d, uint8_t* __restrict__ u,
-                                                    int64_t n, PMapArgs pm) {
-  __shared__ __attribute__((aligned(16))) uint8_t tab[kPTabBytes + kPThrBytes];
-  ptab_build(tab, threadIdx.x, 256, pm);
+                                                    int64_t n, PMapArgs pm, const uint8_t* ptab) {
+  __shared__ __attribute__((aligned(16))) uint8_t tab[kPTabTotal];   // the kernel's only LDS: address 0
+  ptab_copy<4>(ptab, tab);
+  wait_lds_dma();
   __syncthreads();
   const int64_t groups = (n + 31) / 32;
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -974,10 +968,11 @@ void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipS
   else k_int4_tile_dump<64><<<1, 128, 0, st>>>(a, t);
 }
 
-void launch_pmap_probe(const float* d, uint8_t* u, int64_t n, const PMapArgs& pm, hipStream_t st) {
+void launch_pmap_probe(const float* d, uint8_t* u, int64_t n, const PMapArgs& pm, const uint8_t* ptab,
+                       hipStream_t st) {
   if (n <= 0) return;
   const int64_t blocks = ((n + 31) / 32 + 255) / 256;
-  k_pmap_probe<<<(unsigned)(blocks < 2048 ? blocks : 2048), 256, 0, st>>>(d, u, n, pm);
+  k_pmap_probe<<<(unsigned)(blocks < 2048 ? blocks : 2048), 256, 0, st>>>(d, u, n, pm, ptab);
 }
 
 void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {

@@ -42,6 +42,17 @@ struct VQuantArgs {
 // values above X_k (the table then cannot decide, and the kernel compares
 // y = x / 8 with ythr[k] = X_k / 8, both exact).
 constexpr int kPTabEntries = 20112;   // table bytes: top + 1 <= this for P = 15 and 7
+// The table as the kernels hold it in LDS (at address 0): kPTabBytes bytes
+// of entries, then 16 records of 8 bytes.  The host builds it once per plan
+// (pmap_table in ra_host.cpp) and uploads it with the RoPE tables; every
+// workgroup copies it into LDS.  Entry of address a (cell j = top - a): u,
+// the number of X_k whose cell lies above j plus the X_k whose cell is j
+// when that cell holds nothing above X_k, as the e4m3 byte of u; a cell that
+// holds X_k and values above it is marked 0x80 | k.  Record k: X_k / 8
+// (binary32), then the e4m3 bytes of k and k + 1 and two zero bytes.
+constexpr int kPTabBytes = (kPTabEntries + 15) & ~15;
+constexpr int kPThrBytes = 16 * 8;
+constexpr int kPTabTotal = kPTabBytes + kPThrBytes;   // a multiple of 16
 struct PMapArgs {
   int cell[15];
   float ythr[15];
@@ -64,6 +75,7 @@ struct AttnArgs {
   int p_mode;         // 0: range-optimized P (u = round(15 p), code u - 8); 1: symmetric (u = code = round(7 p))
   int v_hadamard;     // V codes are of V H (H = Walsh-Hadamard / sqrt D): the output is multiplied by H
   PMapArgs pm;        // int4 path
+  const uint8_t* ptab; // int4 path: the P-map table (kPTabTotal bytes, 16-byte aligned)
   uint32_t* row_dbg;  // row fingerprints of the parity variant of the int4 kernel ([B*H*N][4]), else null
 };
 
@@ -82,7 +94,8 @@ void launch_bf16_prologue(const QKPrologueArgs& qa, const VQuantArgs& vq, int D,
 void launch_int4_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
 void launch_int4_tile_dump(const AttnArgs& a, const TileDumpArgs& t, int D, hipStream_t st);
 void launch_int4_attn_rowdbg(const AttnArgs& a, int D, int B, hipStream_t st);
-void launch_pmap_probe(const float* d, uint8_t* u, int64_t n, const PMapArgs& pm, hipStream_t st);
+void launch_pmap_probe(const float* d, uint8_t* u, int64_t n, const PMapArgs& pm, const uint8_t* ptab,
+                       hipStream_t st);
 void launch_bf16_attn(const AttnArgs& a, int D, bool out_bf16, int B, hipStream_t st);
 void launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 
