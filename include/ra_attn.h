@@ -24,9 +24,10 @@
  *     (w fastest).  Input dtype bf16 or f32; output dtype f32 or bf16.
  *   * All device pointers must be 16-byte aligned.
  *   * The caller owns q, k, v, o and the workspace; the library never frees
- *     them.  A plan owns only its RoPE tables (host copy, plus one small
- *     device copy per GPU, made by ra_plan_create on the device current then
- *     and by ra_plan_upload on any other).  The forward entry points
+ *     them.  A plan owns only its tables: the RoPE cos/sin tables and the
+ *     byte table of the P map (host copy, plus one small device copy per
+ *     GPU, made by ra_plan_create on the device current then and by
+ *     ra_plan_upload on any other).  The forward entry points
  *     (ra_attn_fwd, ra_attn_prologue, ra_attn_main, ra_attn_fwd_simple once
  *     its plan exists) allocate nothing and never synchronise with the
  *     host, so they may be captured into a HIP graph.
@@ -115,8 +116,9 @@ ra_status ra_opts_default(ra_opts* opts);
 
 /* Validate shape/opts, build the RoPE cos/sin tables on the host (binary64
  * angles, +pi/4 per pair for the merged Interleaved rotation, rounded to
- * binary32) and the P map's thresholds (Sec. 4.2), and, when a GPU is
- * present, copy the tables to the current device (one small allocation and
+ * binary32), the P map's thresholds (Sec. 4.2) and the byte table the INT4
+ * kernels look the P codes up in, and, when a GPU is present, copy the
+ * tables to the current device (one small allocation and
  * a synchronous copy; RA_ERR_OOM / RA_ERR_HIP if that fails, and then no
  * plan is returned).  *out receives a plan to be destroyed with
  * ra_plan_destroy. */
@@ -229,7 +231,9 @@ ra_status ra_debug_tile(ra_plan plan, void* workspace, size_t workspace_bytes,
  * rounding boundary, and operand packing -- on n exponents d (device, f32,
  * d = log2 p <= 0) -> u (device, u8): u = round(15 2^d) = code + 8 for
  * p_mode 0, u = round(7 2^d) = code for p_mode 1.  p_mode outside {0, 1}
- * returns RA_ERR_INVALID_ARG.  Enqueue only. */
+ * returns RA_ERR_INVALID_ARG.  The table is the one plans upload; its
+ * first use per device and mode allocates and copies it synchronously
+ * (kept until the process ends); later calls only enqueue. */
 ra_status ra_debug_pmap(const float* d, uint8_t* u, int64_t n, int32_t p_mode, hipStream_t stream);
 
 /* Stage 2 of an INT4 plan with f32 output (workspace filled by stage 1), run
