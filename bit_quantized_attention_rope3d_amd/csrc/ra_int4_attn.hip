@@ -26,8 +26,10 @@
 //   * P codes come straight out of the accumulator registers: the exponent
 //     d = f32(S c - m) of each score (one FMA) is turned into a table index
 //     j = rint(-4096 d) by a multiply into the fp32 subnormal range (whose
-//     bit pattern is then the rounded index), and looked up in a 32 KB byte
-//     table of u = round(15 2^d) as e4m3 at LDS address 0.  Fifteen table
+//     bit pattern is then the rounded index), and looked up in a 20 KB byte
+//     table of u = round(15 2^d) as e4m3 at LDS address 0 (stored in
+//     reverse, built once per plan on the host and copied into LDS by each
+//     workgroup).  Fifteen table
 //     cells hold a rounding boundary of 15 2^d inside them; their entries
 //     are marked, and the few scores that land in one are decided exactly by
 //     an fp32 compare of d against the boundary.  Two byte permutes and an
