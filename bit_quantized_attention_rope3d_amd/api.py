@@ -262,6 +262,18 @@ def pmap_thresholds(p_mode: int = 0) -> np.ndarray:
     return T
 
 
+def pmap_table(p_mode: int = 0):
+    """The byte table the INT4 kernels look P codes up in (entries, then 16
+    8-byte records; see ra_pmap_table) and its top cell."""
+    buf = np.zeros(RA_PMAP_TABLE_BYTES, np.uint8)
+    top = ctypes.c_int32(0)
+    check(lib().ra_pmap_table(int(p_mode), buf.ctypes.data_as(ctypes.c_void_p), buf.size, ctypes.byref(top)),
+          "ra_pmap_table")
+    return buf, int(top.value)
+
+
+RA_PMAP_TABLE_BYTES = 20240
+
 PEAK_KINDS = {"i8": 0, "fp8": 1, "fp6": 2, "fp6_fp8": 3, "bf16": 4}
 
 

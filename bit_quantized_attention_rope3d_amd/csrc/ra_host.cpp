@@ -98,7 +98,7 @@ ra::PMapArgs pmap_args(int p_mode) {
 
 // e4m3 byte of an integer 0 <= u <= 15 (exact): the PV operand format of u.
 uint8_t e4m3_of_uint(uint32_t u) {
-  if (u == 0) return 0;
+  if (u == 0 || u > 15) return 0;
   int e = 0;
   while ((u >> (e + 1)) != 0) ++e;                       // floor(log2 u) <= 3
   return (uint8_t)(((e + 7) << 3) | ((u << (3 - e)) & 7u));
@@ -120,9 +120,8 @@ std::vector<uint8_t> pmap_table(const ra::PMapArgs& pm) {
     }
     t[a] = (uint8_t)(mark ? mark : e4m3_of_uint(u));
   }
-  for (int k = 0; k < 16; ++k) {
-    const float thr = k < pm.P ? pm.ythr[k] : 0.0f;
-    std::memcpy(&t[ra::kPTabBytes + 8 * k], &thr, 4);
+  for (int k = 0; k < pm.P; ++k) {      // records k >= P stay zero
+    std::memcpy(&t[ra::kPTabBytes + 8 * k], &pm.ythr[k], 4);
     t[ra::kPTabBytes + 8 * k + 4] = e4m3_of_uint((uint32_t)k);
     t[ra::kPTabBytes + 8 * k + 5] = e4m3_of_uint((uint32_t)k + 1);
   }
@@ -618,6 +617,20 @@ ra_status ra_pmap_thresholds(int32_t p_mode, float* T) {
   if (!T) return fail(RA_ERR_INVALID_ARG, "T is null");
   const ra::PMapArgs pm = pmap_args(p_mode);
   for (int k = 0; k < pm.P; ++k) T[k] = -pmap_boundary(pm.P, k);
+  return ok();
+}
+
+static_assert(RA_PMAP_TABLE_BYTES == ra::kPTabTotal, "exported P-map table size");
+
+ra_status ra_pmap_table(int32_t p_mode, uint8_t* out, size_t bytes, int32_t* top) {
+  if (p_mode != 0 && p_mode != 1) return fail(RA_ERR_INVALID_ARG, "p_mode %d is not 0 or 1", p_mode);
+  if (!out || !top) return fail(RA_ERR_INVALID_ARG, "out and top must be non-null");
+  if (bytes < (size_t)ra::kPTabTotal)
+    return fail(RA_ERR_INVALID_ARG, "buffer of %zu bytes is shorter than the %d-byte table", bytes, ra::kPTabTotal);
+  const ra::PMapArgs pm = pmap_args(p_mode);
+  const std::vector<uint8_t> t = pmap_table(pm);
+  std::memcpy(out, t.data(), t.size());
+  *top = pm.top;
   return ok();
 }
 

@@ -48,8 +48,9 @@ constexpr int kPTabEntries = 20112;   // table bytes: top + 1 <= this for P = 15
 // workgroup copies it into LDS.  Entry of address a (cell j = top - a): u,
 // the number of X_k whose cell lies above j plus the X_k whose cell is j
 // when that cell holds nothing above X_k, as the e4m3 byte of u; a cell that
-// holds X_k and values above it is marked 0x80 | k.  Record k: X_k / 8
-// (binary32), then the e4m3 bytes of k and k + 1 and two zero bytes.
+// holds X_k and values above it is marked 0x80 | k.  Record k < P: X_k / 8
+// (binary32), then the e4m3 bytes of k and k + 1 and two zero bytes;
+// records k >= P are zero.
 constexpr int kPTabBytes = (kPTabEntries + 15) & ~15;
 constexpr int kPThrBytes = 16 * 8;
 constexpr int kPTabTotal = kPTabBytes + kPThrBytes;   // a multiple of 16

@@ -65,6 +65,7 @@ _SIGS = {
     "ra_last_error_message": (ctypes.c_char_p, []),
     "ra_plan_upload": (c_i32, [c_void]),
     "ra_pmap_thresholds": (c_i32, [c_i32, c_void]),
+    "ra_pmap_table": (c_i32, [c_i32, c_void, c_size, ctypes.POINTER(c_i32)]),
     "ra_debug_row_digests": (c_i32, [c_void, c_void, c_void, c_size, c_void, c_void]),
     "ra_debug_prologue": (c_i32, [c_void, c_void, c_void, c_void, c_void, c_size,
                                   c_void, c_void, c_void, c_void, c_void, c_void, c_void]),

@@ -204,6 +204,21 @@ const char* ra_last_error_message(void);
  * RA_ERR_INVALID_ARG.  Host only. */
 ra_status ra_pmap_thresholds(int32_t p_mode, float* T);
 
+/* The byte table the INT4 kernels look P codes up in (the one plans
+ * upload), for p_mode 0 or 1: `bytes` must be at least
+ * RA_PMAP_TABLE_BYTES.  Entry a (a = 0 .. 20111) is for the exponent cell
+ * j = top - a, cells of width 2^-12 in x = -d (x rounded as rint(4096 x),
+ * ties to even), and holds the fp8 e4m3 byte of u when every x of the cell
+ * has the same u = #{k : x <= -T[k]}, or 0x80 | k when the cell holds
+ * -T[k] and values above it; entries past top are 0.  Behind the entries,
+ * at byte 20112, 16 records of 8 bytes: record k < P holds -T[k] / 8
+ * (binary32) and the e4m3 bytes of k and k + 1; records k >= P are zero.
+ * *top receives top.
+ * Null arguments, a short buffer or p_mode outside {0, 1} return
+ * RA_ERR_INVALID_ARG.  Host only. */
+#define RA_PMAP_TABLE_BYTES 20240
+ra_status ra_pmap_table(int32_t p_mode, uint8_t* out, size_t bytes, int32_t* top);
+
 /* ---- parity / diagnostics exports (synchronous, test use) ---------------- */
 
 /* Run stage 1 of an INT4 plan into `workspace`, wait for it, and copy the
