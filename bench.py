@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-accuracy", action="store_true",
                     help="skip the error of sampled rows against the oracle and fp64 attention")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-plain", action="store_true",
+                    help="skip the INT4 timing on plain (outlier-free) inputs of the same shape")
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip the sustained MFMA throughput probe")
     ap.add_argument("--main-only-steps", type=int, default=0,
@@ -392,6 +394,32 @@ def main():
         del wsb, outb
         pb.close()
 
+    # The same shape on plain N(0,1) inputs (no outlier channels, diffuse
+    # attention): how the INT4 kernel's speed depends on the inputs.
+    res_plain = None
+    if not args.no_plain and args.inputs != "plain":
+        wp = inputs.with_inputs(inputs.get(args.workload), "plain")
+        qp, kp, vp = inputs.generate_device(wp, wp.seed)
+        outp = p4.empty_out()
+
+        def stepp(e):
+            e[0].record(stream)
+            p4.prologue(qp, kp, vp, ws4, stream)
+            e[1].record(stream)
+            p4.main(outp, ws4, stream)
+            e[2].record(stream)
+
+        log("timing int4 on plain inputs x%d" % args.steps)
+        for _ in range(args.warmup):
+            p4.forward(qp, kp, vp, out=outp, workspace=ws4)
+        totalp, prop, mainp, _ = time_steps(stepp, args.steps, stream)
+        msp = totalp / args.steps
+        res_plain = dict(ms_per_step=msp, main_ms=float(np.mean(mainp)), prologue_ms=float(np.mean(prop)),
+                         value=ops / (msp * 1e-3) / 1e12, pct_int8_peak=100.0 * ops / (msp * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                         note="same shape and plan, N(0,1) Q/K/V with no outlier channels drawn on the device "
+                              "(torch Philox, seed %d); not the headline configuration" % wp.seed)
+        del qp, kp, vp, outp
+
     # Prologue: algorithmic bytes (bf16 Q, K, V read once; Q, K and V codes
     # written as 6-bit fp6).
     E = w.batch * w.tokens * w.heads * w.head_dim
@@ -433,6 +461,7 @@ def main():
         "hbm_copy_gbs": copy_gbs,
         "bf16_fallback": res_bf16,
         "speedup_vs_bf16": (res_bf16["ms_per_step"] / ms4) if res_bf16 else None,
+        "plain_inputs": res_plain,
         "wall_s_timed_int4": wall4,
         "roofline": roof,
         "sustained_mfma": sustained,
